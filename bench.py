@@ -1,0 +1,229 @@
+"""Benchmark: GEMM TFLOPS of pgemm on one MI355X, with roofline and CPU baseline.
+
+One step = one call C <- alpha*A*B + beta*C through the C ABI on inputs that
+are already resident in HBM.  W untimed warmup steps, then K timed steps
+bracketed by torch.cuda.synchronize(); each timed launch is also bracketed by
+HIP events on the stream it is launched on, which gives the kernel's own
+average duration for the roofline figure.
+
+Prints ONE JSON line.  ``value`` is the whole-job throughput in TFLOPS
+(2*M*N*K per step / wall time per step).  ``roofline`` compares the GEMM
+kernel's event-timed throughput with MI355X's dense fp32 (or fp64) matrix
+peak.  ``cpu_baseline`` times the CPU oracle (test infrastructure, built
+from oracle/oracle.c) on a bounded sample of the same workload: the first J
+columns of C, with J chosen for roughly 10-20 s of CPU work; the same sample
+also checks the GPU's first output against the oracle.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--secondary NAME ...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gemm_inputs as gi  # noqa: E402
+
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}  # MI355X dense matrix peaks
+HBM_PEAK_GBS = 8000.0
+METRIC = "GEMM TFLOPS (fp32, M=N=K=2048/8192) and % of MI355X fp32 matrix peak"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sgemm_sweep_8192")
+    ap.add_argument("--secondary", nargs="*", default=["sgemm_2048"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Resident:
+    """A workload's operands on the GPU, plus a launcher bound to them."""
+
+    def __init__(self, name):
+        import torch
+        import precision_gemm_02_amd as pg
+        self.name = name
+        self.p = p = gi.workload(name)
+        self.dt = "f32" if p.dtype == np.float32 else "f64"
+        self.A = torch.from_numpy(p.A).cuda()
+        self.B = torch.from_numpy(p.B).cuda()
+        self.C0 = torch.from_numpy(p.C).cuda()
+        self.C = self.C0.clone()
+        self.pg = pg
+        if p.rowmajor:   # lecture form: C^T = B^T A^T, column-major (n x m)
+            self.args = (p.n, p.m, p.k, p.alpha, self.B.data_ptr(), p.ldb, self.A.data_ptr(),
+                         p.lda, p.beta, self.C.data_ptr(), p.ldc)
+        else:
+            self.args = (p.m, p.n, p.k, p.alpha, self.A.data_ptr(), p.lda, self.B.data_ptr(),
+                         p.ldb, p.beta, self.C.data_ptr(), p.ldc)
+        sel = pg.select_f32 if self.dt == "f32" else pg.select_f64
+        self.variant = pg.variants().get(sel(*self.args), "none")
+        self.flops = 2.0 * p.m * p.n * p.k
+        self.stream = torch.cuda.current_stream()
+
+    def launch(self):
+        if self.p.rowmajor:
+            p = self.p
+            self.pg.matmat_f64(p.lda, p.ldb, p.ldc, self.A.data_ptr(), self.B.data_ptr(),
+                               self.C.data_ptr(), p.m, p.k, p.n, self.stream)
+        elif self.dt == "f32":
+            self.pg.gemm_f32(*self.args, stream=self.stream)
+        else:
+            self.pg.gemm_f64(*self.args, stream=self.stream)
+
+    def reset_c(self):
+        self.C.copy_(self.C0)
+
+    def algorithmic_bytes(self):
+        p = self.p
+        s = 4 if self.dt == "f32" else 8
+        return s * (p.m * p.k + p.k * p.n + p.m * p.n * (1 + (p.beta != 0)))
+
+
+def time_workload(r: Resident, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        r.launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(r.stream)
+        r.launch()
+        e.record(r.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in ev]
+    return wall / steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms))
+
+
+def roofline(r: Resident, kern_ms_mean: float):
+    achieved = r.flops / (kern_ms_mean * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[r.dt]
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": r.variant, "kernel_ms_mean": round(kern_ms_mean, 4)}
+
+
+def cpu_baseline(p, first_out: np.ndarray, seconds: float):
+    """Oracle on the first J columns of problem p; also checks the GPU's first
+    output on those columns."""
+    import oracle
+    oracle.build(force=False)
+    cores = oracle.num_threads()
+    if p.rowmajor:
+        raise ValueError("cpu baseline is defined for the column-major workloads")
+
+    def run(cols):
+        t0 = time.perf_counter()
+        R = oracle.gemm(p.m, cols, p.k, p.alpha, p.A, p.lda, p.B, p.ldb, p.beta, p.C, p.ldc,
+                        dtype=p.dtype)
+        return R, time.perf_counter() - t0
+
+    probe = min(p.n, 16)
+    _, tp = run(probe)
+    cols = int(min(p.n, max(probe, probe * seconds / max(tp, 1e-6))))
+    R, dt = run(cols)
+    flops = 2.0 * p.m * cols * p.k
+    got = first_out[:, :cols].astype(np.float64)
+    D = got - R
+    rel = float(np.linalg.norm(D) / np.linalg.norm(R))
+    maxabs = float(np.max(np.abs(D)))
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "first %d of %d columns of C (%dx%dx%d, %.1f GFLOP), OMP threads=%d, "
+                      "affinity cpus=%d" % (cols, p.n, p.m, cols, p.k, flops / 1e9, cores,
+                                            len(os.sched_getaffinity(0))),
+            "sample_parity": {"max_abs": maxabs, "rel_fro": rel,
+                              "ok": bool(maxabs <= 1e-6 * p.k and rel <= 1e-5)}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the GEMM is not sharded across GPUs in this "
+              "library (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    log("generating", args.workload)
+    r = Resident(args.workload)
+    log("variant", r.variant)
+    # first call on the pristine C: kept for the CPU sample check
+    r.launch()
+    torch.cuda.synchronize()
+    first_out = None
+    if not args.no_cpu_baseline and not r.p.rowmajor:
+        p = r.p
+        ncol = min(p.n, 4096)
+        first_out = r.C[: p.ldc * ncol].view(ncol, p.ldc)[:, : p.m].t().cpu().numpy()
+    r.reset_c()
+    ms_step, kern_mean, kern_med = time_workload(r, args.steps, args.warmup)
+    value = r.flops / (ms_step * 1e-3) / 1e12
+    log("%s: %.3f ms/step, kernel mean %.3f ms -> %.2f TFLOPS" % (r.name, ms_step, kern_mean,
+                                                                   value))
+    p = r.p
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": r.dt, "data": "synthetic",
+        "config": {"workload": r.name, "m": p.m, "n": p.n, "k": p.k, "lda": p.lda,
+                   "ldb": p.ldb, "ldc": p.ldc, "alpha": p.alpha, "beta": p.beta,
+                   "layout": "row-major (operand swap)" if p.rowmajor else "column-major",
+                   "variant": r.variant, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / PEAK_TFLOPS[r.dt], 2),
+        "roofline": roofline(r, kern_mean),
+    }
+    main_problem = r.p
+    secondary = []
+    for name in args.secondary:
+        if name == args.workload:
+            continue
+        del r
+        torch.cuda.empty_cache()
+        r2 = Resident(name)
+        steps2 = max(args.steps, 20)
+        ms2, km2, _ = time_workload(r2, steps2, args.warmup)
+        v2 = r2.flops / (ms2 * 1e-3) / 1e12
+        log("%s: %.3f ms/step, kernel mean %.3f ms -> %.2f TFLOPS" % (name, ms2, km2, v2))
+        secondary.append({"workload": name, "value": round(v2, 3), "unit": "TFLOPS",
+                          "ms_per_step": round(ms2, 4), "steps": steps2, "dtype": r2.dt,
+                          "pct_of_peak": round(100 * v2 / PEAK_TFLOPS[r2.dt], 2),
+                          "roofline": roofline(r2, km2)})
+        r = r2
+    if secondary:
+        out["secondary"] = secondary
+    if first_out is not None:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(main_problem, first_out, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

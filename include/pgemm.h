@@ -1,0 +1,118 @@
+/*
+ * pgemm -- dense matrix multiply C <- alpha*A*B + beta*C for AMD Instinct
+ * MI355X (gfx950), fp32 and fp64, column-major with leading dimensions.
+ *
+ * Plain C ABI: device pointers, sizes, scalars and an opaque HIP stream.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Column-major, neither operand transposed, as in the SGEMM study
+ *   "optimizing-sgemm-on-nvidia-turing-gpus" (introduction).  Element (i, j)
+ *   of a matrix X with leading dimension ldx is X[i + j*ldx].  A is m x k,
+ *   B is k x n, C is m x n.  Only the logical block is read or written; the
+ *   padding rows between the logical extent and the leading dimension are
+ *   never read (A, B) and never written (C).
+ * Memory.  A, B, C are DEVICE pointers on the current HIP device, owned by
+ *   the caller.  The library allocates nothing per call and keeps no state
+ *   besides read-only kernel code.  C must not overlap A or B; A may equal B.
+ * Stream.  `stream` is a hipStream_t passed as void*; NULL means the default
+ *   stream.  Every call is stream-ordered and asynchronous: it returns after
+ *   enqueueing work; the caller synchronizes.
+ * Semantics (BLAS convention where the pages are silent).
+ *   m == 0 or n == 0: nothing is touched, returns 0.
+ *   k == 0 or alpha == 0: C <- beta*C; A and B are not read (may be NULL).
+ *   beta == 0: C is write-only (NaN or Inf already in C does not propagate).
+ * Accuracy.  Products and sums are formed in the working precision (fp32 or
+ *   fp64) by matrix-core multiply-accumulate; the summation order differs
+ *   from a sequential loop, so results are not bitwise equal to one, but a
+ *   given build is deterministic: identical inputs give identical bits.
+ * Errors.  Returns 0 on success.  An invalid argument returns -p, where p is
+ *   the 1-based position of the first offending argument in the signature
+ *   (e.g. -6 for a bad lda in gemm_f32).  A failed kernel launch returns
+ *   PGEMM_EHIP.  Nothing aborts and nothing prints.  Argument checking
+ *   happens before any HIP call.
+ */
+#ifndef PGEMM_H
+#define PGEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PGEMM_OK 0
+#define PGEMM_EHIP (-100)      /* a HIP launch reported an error */
+#define PGEMM_EVARIANT (-101)  /* unknown kernel variant id */
+
+/*
+ * Single precision.  C(m x n) <- alpha * A(m x k) * B(k x n) + beta * C.
+ *
+ *   m, n, k >= 0                       (arguments 1, 2, 3)
+ *   A: lda >= max(1, m)                (arguments 5, 6)
+ *   B: ldb >= max(1, k)                (arguments 7, 8)
+ *   C: ldc >= max(1, m)                (arguments 10, 11)
+ *   A, B may be NULL only if k == 0 or alpha == 0; C only if m == 0 or n == 0.
+ *
+ * Any leading dimension and any 4-byte-aligned pointer is accepted; 16-byte
+ * alignment of a pointer with a leading dimension that is a multiple of 4
+ * selects the 128-bit load path.
+ */
+int gemm_f32(int m, int n, int k, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc,
+             void *stream);
+
+/*
+ * Double precision, same contract as gemm_f32 with 8-byte elements (the
+ * 128-bit path needs 16-byte pointers and even leading dimensions).
+ */
+int gemm_f64(int m, int n, int k, double alpha, const double *A, int lda,
+             const double *B, int ldb, double beta, double *C, int ldc,
+             void *stream);
+
+/*
+ * The lecture's double-precision matmat interface ("HPC - Lecture 13 -
+ * MatMat GPU", section "function matmatgpu1"), on device pointers:
+ * ROW-major A (N1 x N2), B (N2 x N3), C (N1 x N3), row i of X starting at
+ * X + i*ldx, and C <- C + A*B (alpha = beta = 1, as the lecture's kernel
+ * starts each dot product from the old C value).
+ *
+ * A row-major matrix is the column-major storage of its transpose, so this is
+ * gemm_f64(N3, N1, N2, 1, B, ldb, A, lda, 1, C, ldc, stream): no data moves.
+ *   lda >= max(1, N2), ldb >= max(1, N3), ldc >= max(1, N3)   (args 1, 2, 3)
+ *   N1, N2, N3 >= 0                                            (args 7, 8, 9)
+ * Error codes refer to this signature's argument positions.
+ */
+int matmat_f64(int lda, int ldb, int ldc, const double *A, const double *B,
+               double *C, int N1, int N2, int N3, void *stream);
+
+/* Static text for a status code returned by any entry point. */
+const char *pgemm_status_string(int status);
+
+/*
+ * Diagnostics.  pgemm_select_f32 / pgemm_select_f64 return the kernel
+ * variant id the library would launch for these arguments (host logic only,
+ * no HIP call), or a negative status for invalid arguments, or 0 for calls
+ * that launch no GEMM kernel (quick return or the beta-scaling path).
+ * Variant ids are positive; pgemm_variant_name() describes one (NULL if the
+ * id is unknown).  gemm_f32_variant / gemm_f64_variant run the GEMM with a
+ * forced variant (same contract as gemm_f32 / gemm_f64, plus
+ * PGEMM_EVARIANT for an unknown id or one of the other precision); they let
+ * tests cover every compiled tile configuration.
+ */
+int pgemm_select_f32(int m, int n, int k, float alpha, const float *A, int lda,
+                     const float *B, int ldb, float beta, const float *C, int ldc);
+int pgemm_select_f64(int m, int n, int k, double alpha, const double *A, int lda,
+                     const double *B, int ldb, double beta, const double *C, int ldc);
+const char *pgemm_variant_name(int variant);
+int pgemm_num_variants(void);
+int gemm_f32_variant(int variant, int m, int n, int k, float alpha, const float *A,
+                     int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                     void *stream);
+int gemm_f64_variant(int variant, int m, int n, int k, double alpha, const double *A,
+                     int lda, const double *B, int ldb, double beta, double *C, int ldc,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGEMM_H */

@@ -1,0 +1,203 @@
+"""pgemm: C <- alpha*A*B + beta*C on AMD MI355X (gfx950), fp32 and fp64.
+
+Thin ctypes binding over ``libpgemm.so`` (the C ABI declared in
+``include/pgemm.h``).  Every step of the computation runs in the library's
+HIP kernels; this module only turns tensors or integer device addresses into
+pointers, leading dimensions and a stream handle.  PyTorch is used only for
+device memory and the current stream.
+
+Functions with the C names take the C arguments (A, B, C may be torch tensors
+on the GPU or integer device addresses; ``stream`` defaults to torch's
+current stream).  ``gemm(A, B, C, alpha, beta)`` takes 2-D tensors and reads
+the layout from their strides: a column-major view (stride (1, ld)) is used
+as is; a row-major tensor (stride (ld, 1)) is served by the operand swap
+C^T = B^T A^T, which moves no data.
+
+The library must be built (``python -m precision_gemm_02_amd.build``); if it
+is missing, importing this package raises ImportError.  There is no CPU or
+eager fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpgemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libpgemm.so is not built; run `python -m precision_gemm_02_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+# PyTorch-ROCm ships its own HIP runtime with the same SONAME as the system
+# one (libamdhip64.so.7).  Loading torch first makes the dynamic linker bind
+# libpgemm.so to that already-loaded runtime, so that device pointers and
+# stream handles from torch are valid in the library.  Two runtimes in one
+# process would make every torch stream handle foreign to the library.
+import torch as _torch  # noqa: E402,F401  (load order matters)
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+_lib = ctypes.CDLL(LIB_PATH)
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process (%s); import torch before "
+                      "anything that loads /opt/rocm's libamdhip64" %
+                      ", ".join(sorted(_hip_runtimes_mapped())))
+
+_i, _f, _d, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+_lib.gemm_f32.argtypes = [_i, _i, _i, _f, _vp, _i, _vp, _i, _f, _vp, _i, _vp]
+_lib.gemm_f64.argtypes = [_i, _i, _i, _d, _vp, _i, _vp, _i, _d, _vp, _i, _vp]
+_lib.matmat_f64.argtypes = [_i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp]
+_lib.gemm_f32_variant.argtypes = [_i] + _lib.gemm_f32.argtypes
+_lib.gemm_f64_variant.argtypes = [_i] + _lib.gemm_f64.argtypes
+_lib.pgemm_select_f32.argtypes = [_i, _i, _i, _f, _vp, _i, _vp, _i, _f, _vp, _i]
+_lib.pgemm_select_f64.argtypes = [_i, _i, _i, _d, _vp, _i, _vp, _i, _d, _vp, _i]
+_lib.pgemm_status_string.argtypes = [_i]
+_lib.pgemm_status_string.restype = ctypes.c_char_p
+_lib.pgemm_variant_name.argtypes = [_i]
+_lib.pgemm_variant_name.restype = ctypes.c_char_p
+for _name in ("gemm_f32", "gemm_f64", "matmat_f64", "gemm_f32_variant", "gemm_f64_variant",
+              "pgemm_select_f32", "pgemm_select_f64", "pgemm_num_variants"):
+    getattr(_lib, _name).restype = _i
+
+PGEMM_OK = 0
+PGEMM_EHIP = -100
+PGEMM_EVARIANT = -101
+
+EXPORTS = ("gemm_f32", "gemm_f64", "matmat_f64", "pgemm_status_string",
+           "pgemm_select_f32", "pgemm_select_f64", "pgemm_variant_name",
+           "pgemm_num_variants", "gemm_f32_variant", "gemm_f64_variant")
+
+
+class PgemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: status %d (%s)" % (where, status, status_string(status)))
+        self.status = status
+
+
+def library():
+    """The loaded ctypes library (for callers that want raw status codes)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.pgemm_status_string(status).decode()
+
+
+def _addr(x):
+    """Device address of a tensor (its data pointer) or an int; None -> NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, where):
+    if status != PGEMM_OK:
+        raise PgemmError(status, where)
+
+
+def gemm_f32(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """C <- alpha*A*B + beta*C, fp32, column-major (see include/pgemm.h)."""
+    _check(_lib.gemm_f32(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                         _stream(stream)), "gemm_f32")
+
+
+def gemm_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """C <- alpha*A*B + beta*C, fp64, column-major (see include/pgemm.h)."""
+    _check(_lib.gemm_f64(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                         _stream(stream)), "gemm_f64")
+
+
+def matmat_f64(lda, ldb, ldc, A, B, C, N1, N2, N3, stream=None):
+    """Row-major C(N1 x N3) += A(N1 x N2) * B(N2 x N3), fp64 (lecture form)."""
+    _check(_lib.matmat_f64(lda, ldb, ldc, _addr(A), _addr(B), _addr(C), N1, N2, N3,
+                           _stream(stream)), "matmat_f64")
+
+
+def gemm_f32_variant(variant, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    _check(_lib.gemm_f32_variant(variant, m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                 _addr(C), ldc, _stream(stream)), "gemm_f32_variant")
+
+
+def gemm_f64_variant(variant, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    _check(_lib.gemm_f64_variant(variant, m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                 _addr(C), ldc, _stream(stream)), "gemm_f64_variant")
+
+
+def select_f32(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
+    return _lib.pgemm_select_f32(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                 _addr(C), ldc)
+
+
+def select_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
+    return _lib.pgemm_select_f64(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                 _addr(C), ldc)
+
+
+def variants():
+    """{id: name} of every compiled kernel variant."""
+    out = {}
+    for v in range(1, _lib.pgemm_num_variants() + 1):
+        out[v] = _lib.pgemm_variant_name(v).decode()
+    return out
+
+
+def _layout(t):
+    """('col', ld) for a column-major 2-D view, ('row', ld) for row-major."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    r, c = t.shape
+    s0, s1 = t.stride()
+    if s0 == 1 and (c <= 1 or s1 >= max(1, r)):
+        return "col", max(s1, max(1, r)) if c > 1 else max(1, r)
+    if s1 == 1 and (r <= 1 or s0 >= max(1, c)):
+        return "row", max(s0, max(1, c)) if r > 1 else max(1, c)
+    raise ValueError("tensor with strides %s is neither column- nor row-major" % (t.stride(),))
+
+
+def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """C <- alpha*A@B + beta*C in place, for GPU tensors of one dtype.
+
+    All three tensors must share one layout: column-major views (e.g.
+    ``X.t().contiguous().t()`` or a slice of one with padding) or row-major
+    (contiguous) tensors.  Row-major uses the operand swap C^T = B^T A^T.
+    """
+    import torch
+    if not (A.dtype == B.dtype == C.dtype) or A.dtype not in (torch.float32, torch.float64):
+        raise TypeError("A, B, C must all be float32 or all float64")
+    m, k = A.shape
+    k2, n = B.shape
+    if k2 != k or tuple(C.shape) != (m, n):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                              tuple(C.shape)))
+    la, lb, lc = _layout(A), _layout(B), _layout(C)
+    fn = gemm_f32 if A.dtype == torch.float32 else gemm_f64
+    if la[0] == lb[0] == lc[0] == "col":
+        fn(m, n, k, alpha, A, la[1], B, lb[1], beta, C, lc[1], stream)
+    elif la[0] == lb[0] == lc[0] == "row":
+        fn(n, m, k, alpha, B, lb[1], A, la[1], beta, C, lc[1], stream)
+    else:
+        raise ValueError("A, B and C must share one layout")
+    return C

@@ -1,0 +1,235 @@
+// C ABI of pgemm: argument checks, quick returns, variant choice and launch.
+// Declarations and the full contract are in include/pgemm.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pgemm.h"
+#include "variants.hpp"
+
+namespace pgemm {
+namespace {
+
+// Largest grid the launcher accepts (workgroups); far beyond any problem
+// that fits in device memory.
+constexpr long long kMaxTiles = 1LL << 24;
+
+template <typename T>
+bool aligned16(const T* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+template <typename T>
+bool elem_aligned(const T* p) {
+  return (reinterpret_cast<uintptr_t>(p) % sizeof(T)) == 0;
+}
+
+// Returns 0 or -(1-based position of the first bad argument) in the
+// gemm_f32 / gemm_f64 signature.
+template <typename T>
+int check_args(int m, int n, int k, T alpha, const T* A, int lda, const T* B, int ldb,
+               const T* C, int ldc) {
+  if (m < 0) return -1;
+  if (n < 0) return -2;
+  if (k < 0) return -3;
+  const bool touch_c = m > 0 && n > 0;
+  const bool read_ab = touch_c && k > 0 && alpha != T(0);
+  if (read_ab && (A == nullptr || !elem_aligned(A))) return -5;
+  if (lda < (m > 1 ? m : 1)) return -6;
+  if (read_ab && (B == nullptr || !elem_aligned(B))) return -7;
+  if (ldb < (k > 1 ? k : 1)) return -8;
+  if (touch_c && (C == nullptr || !elem_aligned(C))) return -10;
+  if (ldc < (m > 1 ? m : 1)) return -11;
+  return 0;
+}
+
+// 128-bit path: every row of every operand starts on a 16-byte boundary.
+template <typename T>
+bool vec_ok(const T* A, int lda, const T* B, int ldb, const T* C, int ldc) {
+  constexpr int V = 16 / sizeof(T);
+  return aligned16(A) && aligned16(B) && aligned16(C) && lda % V == 0 && ldb % V == 0 &&
+         ldc % V == 0;
+}
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+struct Tables {
+  const Variant<float>* f32;
+  const Variant<double>* f64;
+  int n32, n64;
+  Tables() { f32 = f32_variants(&n32); f64 = f64_variants(&n64); }
+};
+
+const Tables& tables() {
+  static const Tables t;
+  return t;
+}
+
+// Variant table index for fp32, by problem shape and alignment.
+//  * 256 x 256 tiles (wave tile 128 x 128) once they give at least one tile
+//    per compute unit: the most reuse per byte loaded.
+//  * 128 x 128 tiles otherwise, so that e.g. 2048^2 still fills all 256 CUs.
+int choose_f32(int m, int n, bool vec) {
+  const long long t256 = ceil_div(m, 256) * ceil_div(n, 256);
+  const int big = 0, small = 4;  // rows of the fp32 table
+  return (t256 >= 256 ? big : small) + (vec ? 0 : 1);
+}
+
+int choose_f64(int m, int n, bool vec) {
+  (void)m;
+  (void)n;
+  return vec ? 0 : 1;
+}
+
+template <typename T>
+hipError_t launch_scale(int m, int n, T beta, T* C, int ldc, hipStream_t s) {
+  if (beta == T(1)) return hipSuccess;
+  void* args[] = {&m, &n, &beta, &C, &ldc};
+  const dim3 grid((unsigned)ceil_div(m, 256), (unsigned)(n < 65535 ? n : 65535));
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scale_kernel<T>), grid, dim3(256),
+                         args, 0, s);
+}
+
+template <typename T>
+int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, const T* B,
+        int ldb, T beta, T* C, int ldc, hipStream_t s) {
+  if (ceil_div(m, v.bm) * ceil_div(n, v.bn) > kMaxTiles) return PGEMM_EHIP;
+  GemmArgs<T> g{};
+  g.M = m;
+  g.N = n;
+  g.K = k;
+  g.alpha = alpha;
+  g.beta = beta;
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.group_m = 4;
+  return v.launch(g, s) == hipSuccess ? PGEMM_OK : PGEMM_EHIP;
+}
+
+// Shared body of gemm_f32 / gemm_f64 and their forced-variant forms.
+// forced < 0: choose; otherwise index into this precision's table.
+template <typename T>
+int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, const T* B,
+              int ldb, T beta, T* C, int ldc, void* stream) {
+  const int st = check_args(m, n, k, alpha, A, lda, B, ldb, C, ldc);
+  if (st != 0) return st;
+  if (m == 0 || n == 0) return PGEMM_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0 || alpha == T(0))
+    return launch_scale(m, n, beta, C, ldc, s) == hipSuccess ? PGEMM_OK : PGEMM_EHIP;
+  const bool vec = vec_ok(A, lda, B, ldb, C, ldc);
+  const Variant<T>* table;
+  int count, idx;
+  if constexpr (sizeof(T) == 4) {
+    table = tables().f32;
+    count = tables().n32;
+    idx = choose_f32(m, n, vec);
+  } else {
+    table = tables().f64;
+    count = tables().n64;
+    idx = choose_f64(m, n, vec);
+  }
+  if (forced >= 0) {
+    if (forced >= count) return PGEMM_EVARIANT;
+    idx = forced;
+    if (table[idx].vec && !vec) return PGEMM_EVARIANT;
+  }
+  return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
+}
+
+template <typename T>
+int select_impl(int m, int n, int k, T alpha, const T* A, int lda, const T* B, int ldb,
+                const T* C, int ldc) {
+  const int st = check_args(m, n, k, alpha, A, lda, B, ldb, C, ldc);
+  if (st != 0) return st;
+  if (m == 0 || n == 0 || k == 0 || alpha == T(0)) return 0;
+  const bool vec = vec_ok(A, lda, B, ldb, C, ldc);
+  if constexpr (sizeof(T) == 4) return 1 + choose_f32(m, n, vec);
+  else return 1 + tables().n32 + choose_f64(m, n, vec);
+}
+
+}  // namespace
+}  // namespace pgemm
+
+using namespace pgemm;
+
+extern "C" {
+
+int gemm_f32(int m, int n, int k, float alpha, const float* A, int lda, const float* B,
+             int ldb, float beta, float* C, int ldc, void* stream) {
+  return gemm_impl<float>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f64(int m, int n, int k, double alpha, const double* A, int lda, const double* B,
+             int ldb, double beta, double* C, int ldc, void* stream) {
+  return gemm_impl<double>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+// Row-major X (r x c, ld) is the column-major storage of X^T (c x r, ld), so
+// C^T = B^T A^T is a column-major GEMM with m = N3, n = N1, k = N2.
+int matmat_f64(int lda, int ldb, int ldc, const double* A, const double* B, double* C,
+               int N1, int N2, int N3, void* stream) {
+  const bool touch_c = N1 > 0 && N3 > 0;
+  const bool read_ab = touch_c && N2 > 0;
+  if (lda < (N2 > 1 ? N2 : 1)) return -1;
+  if (ldb < (N3 > 1 ? N3 : 1)) return -2;
+  if (ldc < (N3 > 1 ? N3 : 1)) return -3;
+  if (read_ab && (A == nullptr || !elem_aligned(A))) return -4;
+  if (read_ab && (B == nullptr || !elem_aligned(B))) return -5;
+  if (touch_c && (C == nullptr || !elem_aligned(C))) return -6;
+  if (N1 < 0) return -7;
+  if (N2 < 0) return -8;
+  if (N3 < 0) return -9;
+  return gemm_f64(N3, N1, N2, 1.0, B, ldb, A, lda, 1.0, C, ldc, stream);
+}
+
+const char* pgemm_status_string(int status) {
+  switch (status) {
+    case PGEMM_OK: return "success";
+    case PGEMM_EHIP: return "HIP kernel launch failed";
+    case PGEMM_EVARIANT: return "unknown or inapplicable kernel variant";
+    default: break;
+  }
+  if (status < 0 && status >= -12) return "invalid argument (see the argument position)";
+  return "unknown status";
+}
+
+int pgemm_select_f32(int m, int n, int k, float alpha, const float* A, int lda,
+                     const float* B, int ldb, float beta, const float* C, int ldc) {
+  (void)beta;
+  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc);
+}
+
+int pgemm_select_f64(int m, int n, int k, double alpha, const double* A, int lda,
+                     const double* B, int ldb, double beta, const double* C, int ldc) {
+  (void)beta;
+  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc);
+}
+
+int pgemm_num_variants(void) { return tables().n32 + tables().n64; }
+
+const char* pgemm_variant_name(int variant) {
+  if (variant >= 1 && variant <= tables().n32) return tables().f32[variant - 1].name;
+  const int j = variant - 1 - tables().n32;
+  if (j >= 0 && j < tables().n64) return tables().f64[j].name;
+  return nullptr;
+}
+
+int gemm_f32_variant(int variant, int m, int n, int k, float alpha, const float* A, int lda,
+                     const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
+  if (variant < 1 || variant > tables().n32) return PGEMM_EVARIANT;
+  return gemm_impl<float>(variant - 1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f64_variant(int variant, int m, int n, int k, double alpha, const double* A,
+                     int lda, const double* B, int ldb, double beta, double* C, int ldc,
+                     void* stream) {
+  const int j = variant - 1 - tables().n32;
+  if (j < 0 || j >= tables().n64) return PGEMM_EVARIANT;
+  return gemm_impl<double>(j, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+}  // extern "C"

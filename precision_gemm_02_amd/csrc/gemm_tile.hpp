@@ -1,0 +1,407 @@
+// MFMA tile kernel for C <- alpha*A*B + beta*C, column-major, A and B not
+// transposed, on gfx950 (CDNA4).  One template serves fp32 and fp64; the
+// precision enters only through a trait that names the matrix instruction.
+//
+// Design (what the pages' techniques become on CDNA4):
+//  * Shared-memory blocking of A and B ("optimizing-sgemm-on-nvidia-turing-
+//    gpus", kernel 2 and the larger tiles of kernels 7-8; "HPC - Lecture 13",
+//    section "Kernel 2: Shared Memory Optimization") becomes an LDS tile of
+//    BM x BK of A and BK x BN of B per workgroup.
+//  * 128-bit vector loads (the SGEMM study's float4 step; the "V3.
+//    Vectorized and double buffer" page, measure (1)) become 16-byte global
+//    loads and 16-byte LDS reads and writes.
+//  * Register micro-tiles and warp tiles (SGEMM study, kernels 5, 7 and 9)
+//    become one wave-level tile of RB x CB matrix-core blocks whose
+//    accumulators stay in registers for the whole K loop.
+//  * Double buffering / prefetch (SGEMM study kernel 10; V3 page measure
+//    (2)): two LDS stages; the next K tile is fetched from HBM into registers
+//    while the current one feeds the matrix cores, then written to the other
+//    stage; one workgroup barrier per K tile.
+//  * Bank-conflict fixes (V3 page, sections V3.1 and V3.2): column-major A
+//    arrives m-contiguous and is stored as As[k][m] with no transpose, so its
+//    16-byte writes and reads are contiguous per lane group; B arrives
+//    k-contiguous and is stored as Bs[n][k] with an XOR swizzle of its 16-byte
+//    chunks chosen so that the row-strided operand reads and the stores both
+//    touch distinct banks.
+//  * Edge tiles ("HPC - Lecture 13", kernel 2's note that a general version
+//    must handle inactive threads): out-of-range rows, columns and K entries
+//    load as zero and never touch memory; stores are predicated.
+//
+// Operand permutations that let one 16-byte LDS read feed several MFMAs
+// without changing the result:
+//  * rows: within a super-block of W row blocks, MFMA row i of block b' is
+//    tile row W*i + b', so lane l reads W consecutive rows of As at once;
+//  * k: within a group of KG = KPER*V inner indices, the matrix instruction's
+//    k slot g (lanes g*MB .. g*MB+MB-1) at step s takes inner index V*g + s,
+//    so lane l reads V consecutive k of Bs at once.  A uses the same mapping,
+//    so every product A(i,k)*B(k,j) is formed exactly once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pgemm {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef double doublex2 __attribute__((ext_vector_type(2)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x2f32: 32x32 block, 2 inner indices per instruction.
+struct TraitF32 {
+  using T = float;
+  using chunk_t = floatx4;           // one 16-byte chunk
+  using acc_t = floatx16;            // accumulators of one block, per lane
+  static constexpr int V = 4;        // elements per 16-byte chunk
+  static constexpr int MB = 32;      // block edge
+  static constexpr int KPER = 2;     // inner indices per instruction
+  static constexpr int NACC = 16;    // accumulator elements per lane
+  // Accumulator register r of lane l holds block row
+  //   8*(r/4) + 4*(l/32) + r%4,  block column l%32
+  // (measured on gfx950).  Registers come in runs of RUN_R consecutive rows;
+  // run j of the lane with inner-index slot `kslot` starts at irow(j, kslot).
+  static constexpr int RUN_R = 4;
+  static __device__ __forceinline__ int irow(int run, int kslot) { return 8 * run + 4 * kslot; }
+  static __device__ __forceinline__ acc_t mfma(T a, T b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// v_mfma_f64_16x16x4f64: 16x16 block, 4 inner indices per instruction.
+struct TraitF64 {
+  using T = double;
+  using chunk_t = doublex2;
+  using acc_t = doublex4;
+  static constexpr int V = 2;
+  static constexpr int MB = 16;
+  static constexpr int KPER = 4;
+  static constexpr int NACC = 4;
+  // Accumulator register r of lane l holds block row (l/16) + 4*r, block
+  // column l%16 (measured on gfx950): runs of one row each.
+  static constexpr int RUN_R = 1;
+  static __device__ __forceinline__ int irow(int run, int kslot) { return kslot + 4 * run; }
+  static __device__ __forceinline__ acc_t mfma(T a, T b, acc_t c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename T>
+struct GemmArgs {
+  int M, N, K;
+  T alpha, beta;
+  const T* A;
+  const T* B;
+  T* C;
+  int lda, ldb, ldc;
+  int tiles_m, tiles_n;
+  int group_m;     // tile rows per raster group
+};
+
+// Workgroup id -> (tile row, tile column).
+// The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn, and
+// each XCD has its own L2.  Give every XCD one contiguous range of tile ids,
+// then walk tiles in groups of `group_m` tile rows so that the workgroups
+// resident on one XCD at the same time share A and B panels in its L2.
+__host__ __device__ inline void map_tile(int wg, int tiles_m, int tiles_n, int group_m,
+                                         int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int xcd = wg & 7, local = wg >> 3;
+  const int base = total >> 3, rem = total & 7;
+  const int t = xcd * base + (xcd < rem ? xcd : rem) + local;
+  const int per_group = group_m * tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * group_m;
+  const int gsize = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+  const int within = t - group * per_group;
+  tm = first_m + within % gsize;
+  tn = within / gsize;
+}
+
+// XOR swizzle of the 16-byte chunks of one Bs row (KC chunks per row).  For
+// any 8 (resp. 16) consecutive rows read at the same logical chunk, the
+// physical chunks fall in distinct 16-byte bank groups of a 128-byte (resp.
+// 256-byte) bank line, and so do the chunks that 8 or 16 consecutive lanes
+// store when they fill consecutive chunks of consecutive rows.
+template <int KC>
+__host__ __device__ inline int swz(int n) {
+  if constexpr (KC == 4) {
+    return (((n >> 1) ^ (n >> 3)) & 1) | (((n >> 2) & 1) << 1);
+  } else if constexpr (KC == 8) {
+    return (n & 7) ^ ((n >> 3) & 1);
+  } else {
+    static_assert(KC == 16, "Bs rows of 4, 8 or 16 chunks");
+    return n & 15;
+  }
+}
+
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+struct TileCfg {
+  using T = typename TR::T;
+  static constexpr int NT = WGM * WGN * 64;           // threads per workgroup
+  static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
+  static constexpr int RB = WM / TR::MB, CB = WN / TR::MB;
+  static constexpr int V = TR::V;
+  static constexpr int W = RB < V ? RB : V;           // rows per lane per LDS read
+  static constexpr int SB = RB / W;                   // row super-blocks
+  static constexpr int KG = TR::KPER * V;             // inner indices per group
+  static constexpr int KC = BK / V;                   // chunks per Bs row
+  static constexpr int A_STAGE = BK * BM, B_STAGE = BN * BK;  // elements
+  static constexpr int A_CHUNKS = A_STAGE / V, B_CHUNKS = B_STAGE / V;
+  static constexpr int A_LOADS = A_CHUNKS / NT, B_LOADS = B_CHUNKS / NT;
+  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * (int)sizeof(T);
+  static_assert(WM * WGM == BM && WN * WGN == BN, "waves tile the block");
+  static_assert(RB * TR::MB == WM && CB * TR::MB == WN, "blocks tile the wave");
+  static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8, "row blocks");
+  static_assert(BK % KG == 0, "K tile is whole groups");
+  static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "even load split");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
+};
+
+// ---------------------------------------------------------------- loads
+// One 16-byte chunk of V consecutive elements starting at p; element e is
+// in range when e < valid.  valid >= V uses one vector load (VEC) or V
+// scalar loads; out-of-range elements are zero and are never read.
+template <class TR, bool VEC>
+__device__ __forceinline__ typename TR::chunk_t load_chunk(const typename TR::T* p, int valid) {
+  using T = typename TR::T;
+  typename TR::chunk_t v;
+  if (VEC && valid >= TR::V) {
+    v = *reinterpret_cast<const typename TR::chunk_t*>(p);
+  } else {
+#pragma unroll
+    for (int e = 0; e < TR::V; ++e) v[e] = (e < valid) ? p[e] : T(0);
+  }
+  return v;
+}
+
+template <class TR, bool VEC>
+__device__ __forceinline__ typename TR::chunk_t load_chunk_full(const typename TR::T* p) {
+  typename TR::chunk_t v;
+  if constexpr (VEC) {
+    v = *reinterpret_cast<const typename TR::chunk_t*>(p);
+  } else {
+#pragma unroll
+    for (int e = 0; e < TR::V; ++e) v[e] = p[e];
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- kernel
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_tile_kernel(GemmArgs<typename TR::T> g) {
+  using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC>;
+  using T = typename TR::T;
+  using chunk_t = typename TR::chunk_t;
+  using acc_t = typename TR::acc_t;
+  constexpr int V = TR::V, MB = TR::MB, NT = Cfg::NT;
+  constexpr int RB = Cfg::RB, CB = Cfg::CB, W = Cfg::W, SB = Cfg::SB;
+  constexpr int KG = Cfg::KG, KC = Cfg::KC;
+  constexpr int A_LOADS = Cfg::A_LOADS, B_LOADS = Cfg::B_LOADS;
+
+  __shared__ __attribute__((aligned(16))) T lds[2 * (Cfg::A_STAGE + Cfg::B_STAGE)];
+
+  int tm, tn;
+  map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wrow = (wave % WGM) * Cfg::WM, wcol = (wave / WGM) * Cfg::WN;
+  const int M = g.M, N = g.N, K = g.K;
+  const int lda = g.lda, ldb = g.ldb;
+  const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
+
+  // Per-thread load assignment.  Chunk q = tid + i*NT.
+  //  A: column q / (BM/V), rows (q % (BM/V))*V .. +V-1 of the tile.
+  //  B: column q / KC, inner indices (q % KC)*V .. +V-1 of the tile.
+  chunk_t ra[A_LOADS], rb[B_LOADS];
+
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+    if (full_mn && k0 + BK <= K) {
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) {
+        const int q = tid + i * NT;
+        const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
+        ra[i] = load_chunk_full<TR, VEC>(g.A + (size_t)(k0 + kk) * lda + (m0 + mm));
+      }
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int q = tid + i * NT;
+        const int nn = q / KC, kk = (q % KC) * V;
+        rb[i] = load_chunk_full<TR, VEC>(g.B + (size_t)(n0 + nn) * ldb + (k0 + kk));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) {
+        const int q = tid + i * NT;
+        const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
+        const int k = k0 + kk, m = m0 + mm;
+        const int valid = (k < K) ? min(M - m, V) : 0;
+        if (valid > 0) ra[i] = load_chunk<TR, VEC>(g.A + (size_t)k * lda + m, valid);
+        else ra[i] = chunk_t{};
+      }
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int q = tid + i * NT;
+        const int nn = q / KC, kk = (q % KC) * V;
+        const int n = n0 + nn, k = k0 + kk;
+        const int valid = (n < N) ? min(K - k, V) : 0;
+        if (valid > 0) rb[i] = load_chunk<TR, VEC>(g.B + (size_t)n * ldb + k, valid);
+        else rb[i] = chunk_t{};
+      }
+    }
+  };
+
+  auto lstore = [&](int stage) {
+    T* As = lds + stage * (Cfg::A_STAGE + Cfg::B_STAGE);
+    T* Bs = As + Cfg::A_STAGE;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int q = tid + i * NT;
+      const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
+      *reinterpret_cast<chunk_t*>(As + kk * BM + mm) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int q = tid + i * NT;
+      const int nn = q / KC, kc = q % KC;
+      *reinterpret_cast<chunk_t*>(Bs + nn * BK + ((kc ^ swz<KC>(nn)) * V)) = rb[i];
+    }
+  };
+
+  acc_t acc[RB][CB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int c = 0; c < CB; ++c) acc[b][c] = acc_t{};
+
+  // Lane roles in the matrix instruction.
+  const int lrow = lane % MB;   // block row (A) / block column (B) of this lane
+  const int kslot = lane / MB;  // which inner-index slot of the instruction
+
+  auto compute = [&](int stage) {
+    const T* As = lds + stage * (Cfg::A_STAGE + Cfg::B_STAGE);
+    const T* Bs = As + Cfg::A_STAGE;
+#pragma unroll
+    for (int kg = 0; kg < BK; kg += KG) {
+      // B: one 16-byte read per column block gives V consecutive k.
+      chunk_t bv[CB];
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int n = wcol + c * MB + lrow;
+        const int kc = kg / V + kslot;
+        bv[c] = *reinterpret_cast<const chunk_t*>(Bs + n * BK + ((kc ^ swz<KC>(n)) * V));
+      }
+#pragma unroll
+      for (int s = 0; s < V; ++s) {
+        const int k = kg + V * kslot + s;
+        T av[RB];
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          const T* p = As + k * BM + wrow + sb * MB * W + W * lrow;
+          if constexpr (W == 4) {
+            floatx4 t = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[sb * W + e] = t[e];
+          } else if constexpr (W == 2) {
+            typedef T T2 __attribute__((ext_vector_type(2)));
+            T2 t = *reinterpret_cast<const T2*>(p);
+            av[sb * W + 0] = t[0];
+            av[sb * W + 1] = t[1];
+          } else {
+            av[sb] = p[0];
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+          for (int c = 0; c < CB; ++c) acc[b][c] = TR::mfma(av[b], bv[c][s], acc[b][c]);
+      }
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) gload(kt + 1);
+    compute(kt & 1);
+    if (more) lstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue.  A lane's accumulator registers come in runs of RUN_R
+  // consecutive block rows (see the trait).  Block b = sb*W + b' puts block
+  // row i at wave-tile row sb*MB*W + W*i + b', so for fixed (c, sb, run) the
+  // lane owns RUN = RUN_R*W consecutive rows of one column: element o of
+  // that run is register run*RUN_R + o/W of block sb*W + o%W.
+  const T alpha = g.alpha, beta = g.beta;
+  const int ldc = g.ldc;
+  constexpr int RUN = TR::RUN_R * W;
+  constexpr int NRUN = TR::NACC / TR::RUN_R;
+  constexpr bool VEC_C = VEC && (RUN % V == 0);
+#pragma unroll
+  for (int c = 0; c < CB; ++c) {
+    const int col = n0 + wcol + c * MB + lrow;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+#pragma unroll
+      for (int run = 0; run < NRUN; ++run) {
+        const int row = m0 + wrow + sb * MB * W + W * TR::irow(run, kslot);
+        T out[RUN];
+#pragma unroll
+        for (int o = 0; o < RUN; ++o)
+          out[o] = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+        T* pc = g.C + (size_t)col * ldc + row;
+        if (full_mn || (col < N && row + RUN <= M)) {
+          if constexpr (VEC_C) {
+#pragma unroll
+            for (int h = 0; h < RUN / V; ++h) {
+              chunk_t v;
+#pragma unroll
+              for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
+              if (beta != T(0)) {
+                chunk_t cv = *reinterpret_cast<const chunk_t*>(pc + h * V);
+#pragma unroll
+                for (int e = 0; e < V; ++e) v[e] = __builtin_fma(beta, cv[e], v[e]);
+              }
+              *reinterpret_cast<chunk_t*>(pc + h * V) = v;
+            }
+          } else {
+#pragma unroll
+            for (int o = 0; o < RUN; ++o) {
+              T v = out[o];
+              if (beta != T(0)) v = __builtin_fma(beta, pc[o], v);
+              pc[o] = v;
+            }
+          }
+        } else if (col < N) {
+#pragma unroll
+          for (int o = 0; o < RUN; ++o) {
+            if (row + o < M) {
+              T v = out[o];
+              if (beta != T(0)) v = __builtin_fma(beta, pc[o], v);
+              pc[o] = v;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// C <- beta*C on the m x n block (the k == 0 / alpha == 0 path); beta == 0
+// writes zeros without reading C.
+template <typename T>
+__global__ void __launch_bounds__(256) scale_kernel(int M, int N, T beta, T* C, int ldc) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M) return;
+  for (int j = blockIdx.y; j < N; j += gridDim.y) {
+    T* p = C + (size_t)j * ldc + i;
+    *p = (beta == T(0)) ? T(0) : beta * *p;
+  }
+}
+
+}  // namespace pgemm

@@ -1,0 +1,40 @@
+// Internal: the compiled tile configurations of each precision.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_tile.hpp"
+
+namespace pgemm {
+
+template <typename T>
+using LaunchFn = hipError_t (*)(const GemmArgs<T>&, hipStream_t);
+
+template <typename T>
+struct Variant {
+  const char* name;
+  int bm, bn, bk;
+  bool vec;        // needs 16-byte aligned pointers and leading dims
+  LaunchFn<T> launch;
+};
+
+// Launch one tile configuration: one workgroup per BM x BN tile of C.
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
+  using T = typename TR::T;
+  GemmArgs<T> g = a;
+  g.tiles_m = (g.M + BM - 1) / BM;
+  g.tiles_n = (g.N + BN - 1) / BN;
+  if (g.group_m <= 0) g.group_m = 4;
+  void* args[] = {&g};
+  const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(WGM * WGN * 64);
+  return hipLaunchKernel(reinterpret_cast<const void*>(
+                             &gemm_tile_kernel<TR, BM, BN, BK, WGM, WGN, VEC>),
+                         grid, block, args, 0, stream);
+}
+
+// The compiled configurations of each precision, in a fixed order.
+const Variant<float>* f32_variants(int* count);
+const Variant<double>* f64_variants(int* count);
+
+}  // namespace pgemm

@@ -1,0 +1,312 @@
+"""GPU library vs the CPU oracle (needs an MI355X; every test is marked gpu).
+
+Every call goes through the C ABI (``libpgemm.so`` via the thin binding).
+Inputs come from ``gemm_inputs`` (seeded); expected values come only from
+``oracle`` (or, for whole-output checks at the largest size, from Freivalds'
+randomized identity computed with numpy).
+
+Bars:
+  * fp32: max|dC| <= 1e-6*K and ||dC||_F/||R||_F <= 1e-5;
+  * fp64: ||dC||_F/||R||_F <= 1e-12;
+  * exact-integer inputs (entries in {-2..2}, alpha/beta multiples of 1/4):
+    every partial sum is an integer below 2^24, so every summation order is
+    exact and the GPU must equal the oracle bit for bit;
+  * C's leading-dimension padding and the guard margins around every buffer
+    must be bit-identical after the call; A/B padding is NaN.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import gemm_inputs as gi  # noqa: E402
+import oracle  # noqa: E402
+from gpu_util import (DevMat, assert_bitwise, assert_f32_parity, assert_f64_parity,  # noqa: E402
+                      freivalds, logical, sample_indices)
+
+torch = pytest.importorskip("torch")
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+pg = pytest.importorskip("precision_gemm_02_amd")
+
+
+def say(*a):
+    print("[parity]", *a, flush=True)
+
+
+def run_colmajor(p, offset=0, variant=None):
+    """Run problem p (column-major) on the GPU; return (C logical, DevMats)."""
+    dA, dB, dC = DevMat(p.A, offset=offset), DevMat(p.B), DevMat(p.C)
+    if p.dtype == np.float32:
+        fn = pg.gemm_f32 if variant is None else (
+            lambda *a: pg.gemm_f32_variant(variant, *a))
+    else:
+        fn = pg.gemm_f64 if variant is None else (
+            lambda *a: pg.gemm_f64_variant(variant, *a))
+    fn(p.m, p.n, p.k, p.alpha, dA.ptr, p.lda, dB.ptr, p.ldb, p.beta, dC.ptr, p.ldc)
+    torch.cuda.synchronize()
+    dC.assert_untouched_outside(p.m, p.n, p.ldc)
+    dA.assert_untouched_outside(p.m, p.k, p.lda)
+    dB.assert_untouched_outside(p.k, p.n, p.ldb)
+    return logical(dC.storage(), p.m, p.n, p.ldc).copy(), (dA, dB, dC)
+
+
+def oracle_full(p):
+    return oracle.gemm(p.m, p.n, p.k, p.alpha, p.A, p.lda, p.B, p.ldb, p.beta, p.C, p.ldc,
+                       dtype=p.dtype)
+
+
+# ------------------------------------------------------------- workloads
+SMALL_WORKLOADS = ["sgemm_128", "sgemm_2048", "sgemm_sweep_512", "sgemm_sweep_1024",
+                   "sgemm_sweep_2048", "sgemm_sweep_4096", "sgemm_ragged"]
+
+
+@pytest.mark.parametrize("name", SMALL_WORKLOADS)
+def test_workload_full_oracle(name):
+    p = gi.workload(name)
+    say(name, p.m, p.n, p.k, "variant", pg.select_f32(p.m, p.n, p.k, p.alpha, 1 << 20, p.lda,
+                                                       1 << 20, p.ldb, p.beta, 1 << 20, p.ldc))
+    C, _ = run_colmajor(p)
+    R = oracle_full(p)
+    maxabs, rel = assert_f32_parity(C, R, p.k)
+    say(name, "max|dC| %.3g rel %.3g" % (maxabs, rel))
+
+
+def test_workload_8192_sampled_and_freivalds():
+    p = gi.workload("sgemm_sweep_8192")
+    say("8192 generated")
+    C, _ = run_colmajor(p)
+    I, J = sample_indices(p.m, p.n, 4096, seed=5)
+    R = oracle.gemm_entries(p.m, p.n, p.k, p.alpha, p.A, p.lda, p.B, p.ldb, p.beta, p.C,
+                            p.ldc, I, J)
+    D = C[I, J].astype(np.float64) - R
+    assert np.max(np.abs(D)) <= 1e-6 * p.k
+    assert np.linalg.norm(D) / np.linalg.norm(R) <= 1e-5
+    # two whole columns through the full oracle
+    for j0 in (0, p.n - 1):
+        Rc = oracle.gemm(p.m, 1, p.k, p.alpha, p.A, p.lda, p.B[j0 * p.ldb:], p.ldb, p.beta,
+                         p.C[j0 * p.ldc:], p.ldc)
+        assert_f32_parity(C[:, j0:j0 + 1], Rc, p.k)
+    A = logical(p.A, p.m, p.k, p.lda)
+    B = logical(p.B, p.k, p.n, p.ldb)
+    C0 = logical(p.C, p.m, p.n, p.ldc)
+    err = freivalds(C, A, B, C0, p.alpha, p.beta, vectors=3)
+    say("8192 freivalds rel %.3g" % err)
+    assert err <= 1e-5
+
+
+def run_matmat(p):
+    dA, dB, dC = DevMat(p.A), DevMat(p.B), DevMat(p.C)
+    N1, N2, N3 = p.m, p.k, p.n
+    pg.matmat_f64(p.lda, p.ldb, p.ldc, dA.ptr, dB.ptr, dC.ptr, N1, N2, N3)
+    torch.cuda.synchronize()
+    # row-major C (N1 x N3, ldc) is column-major (N3 x N1, ldc)
+    dC.assert_untouched_outside(N3, N1, p.ldc)
+    return gi.logical_rowmajor(dC.storage(), N1, N3, p.ldc).copy()
+
+
+def test_workload_dgemm_rowmajor_sampled_and_freivalds():
+    p = gi.workload("dgemm_rowmajor")
+    assert p.alpha == 1.0 and p.beta == 1.0   # the lecture's C += A*B
+    C = run_matmat(p)
+    N1, N2, N3 = p.m, p.k, p.n
+    I, J = sample_indices(N1, N3, 4096, seed=6)
+    R = oracle.matmat_rowmajor_f64_entries(p.lda, p.ldb, p.ldc, p.A, p.B, p.C, N1, N2, N3,
+                                           I, J)
+    D = C[I, J] - R
+    assert np.linalg.norm(D) / np.linalg.norm(R) <= 1e-12
+    A = gi.logical_rowmajor(p.A, N1, N2, p.lda)
+    B = gi.logical_rowmajor(p.B, N2, N3, p.ldb)
+    C0 = gi.logical_rowmajor(p.C, N1, N3, p.ldc)
+    err = freivalds(C, A, B, C0, 1.0, 1.0, vectors=3)
+    say("dgemm 4096 freivalds rel %.3g" % err)
+    assert err <= 1e-12
+
+
+@pytest.mark.parametrize("N1,N2,N3,pad", [(1, 1, 1, 0), (37, 53, 29, 8), (300, 257, 129, 2),
+                                          (512, 512, 512, 8)])
+def test_matmat_f64_full_oracle(N1, N2, N3, pad):
+    p = gi.make_rowmajor_problem("mm", N1, N2, N3, N2 + pad, N3 + pad, N3 + pad, 1.0, 1.0,
+                                 seed=N1 + N2)
+    C = run_matmat(p)
+    R = oracle.matmat_rowmajor_f64(p.lda, p.ldb, p.ldc, p.A, p.B, p.C, N1, N2, N3)
+    assert_f64_parity(C, R)
+
+
+# --------------------------------------------------- exact-integer, bitwise
+EXACT_SHAPES = [(1, 1, 1), (7, 5, 3), (32, 32, 8), (33, 65, 9), (256, 256, 64),
+                (300, 260, 70), (513, 257, 1023), (129, 700, 31)]
+ALPHA_BETA = [(1.0, 0.0), (1.0, 1.0), (0.75, -1.25), (1.5, 0.5)]
+
+
+def exact_problem(dtype, m, n, k, alpha, beta, lds, seed):
+    lda, ldb, ldc = lds
+    return gi.make_colmajor_problem("exact", dtype, m, n, k, lda, ldb, ldc, alpha, beta,
+                                    seed, dist="i2", c_dist=None if beta == 0 else "i2")
+
+
+def variant_ids(prefix):
+    return [v for v, n in pg.variants().items() if n.startswith(prefix)]
+
+
+def leading_dims(m, k, vec, chunk, t):
+    """Vector variants: multiples of the 16-byte chunk; scalar: odd values."""
+    if vec:
+        up = lambda x: -(-x // chunk) * chunk  # noqa: E731
+        extra = chunk * (t % 2)
+        return up(m) + extra, up(k) + extra, up(m) + 2 * extra
+    return m + 1 + 2 * (t % 2), k + 1, m + 3
+
+
+@pytest.mark.parametrize("variant", variant_ids("f32_") + variant_ids("f64_"),
+                         ids=lambda v: pg.variants()[v])
+def test_every_variant_exact_integer(variant):
+    name = pg.variants()[variant]
+    dtype = np.float32 if name.startswith("f32_") else np.float64
+    chunk = 4 if dtype == np.float32 else 2
+    vec = name.endswith("_vec")
+    for t, (m, n, k) in enumerate(EXACT_SHAPES):
+        alpha, beta = ALPHA_BETA[t % len(ALPHA_BETA)]
+        lds = leading_dims(m, k, vec, chunk, t)
+        p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=100 + t)
+        say(name, (m, n, k), (alpha, beta), "ld", lds)
+        C, _ = run_colmajor(p, variant=variant)
+        assert_bitwise(C, oracle_full(p))
+
+
+@pytest.mark.parametrize("name", ["sgemm_128", "sgemm_2048", "sgemm_sweep_4096",
+                                  "sgemm_ragged"])
+def test_workload_shapes_exact_integer(name):
+    p = gi.workload(name, dist_override="i2")
+    if p.beta == 0:
+        p.C = gi.colmajor(np.full(p.m * p.n, np.nan, np.float32), p.m, p.n, p.ldc,
+                          gi.C_SENTINEL_F32)
+    C, _ = run_colmajor(p)
+    assert_bitwise(C, oracle_full(p))
+
+
+def test_workload_8192_exact_integer_sampled():
+    p = gi.workload("sgemm_sweep_8192", dist_override="i2")
+    C, _ = run_colmajor(p)
+    I, J = sample_indices(p.m, p.n, 8192, seed=7)
+    R = oracle.gemm_entries(p.m, p.n, p.k, p.alpha, p.A, p.lda, p.B, p.ldb, p.beta, p.C,
+                            p.ldc, I, J)
+    assert np.array_equal(C[I, J].astype(np.float64), R)
+
+
+def test_dgemm_rowmajor_exact_integer_sampled():
+    p = gi.workload("dgemm_rowmajor", dist_override="i2")
+    C = run_matmat(p)
+    I, J = sample_indices(p.m, p.n, 4096, seed=8)
+    R = oracle.matmat_rowmajor_f64_entries(p.lda, p.ldb, p.ldc, p.A, p.B, p.C, p.m, p.k,
+                                           p.n, I, J)
+    assert np.array_equal(C[I, J], R)
+
+
+# --------------------------------------------------------- special cases
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_beta_zero_ignores_nan_c(dtype):
+    p = gi.make_colmajor_problem("nanc", dtype, 200, 150, 77, 200, 80, 204, 1.0, 0.0, seed=3)
+    assert np.isnan(logical(p.C, p.m, p.n, p.ldc)).all()
+    C, _ = run_colmajor(p)
+    R = oracle_full(p)
+    if dtype == np.float32:
+        assert_f32_parity(C, R, p.k)
+    else:
+        assert_f64_parity(C, R)
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_alpha_zero_and_k_zero_scale_c(dtype):
+    m, n, ldc = 300, 70, 303
+    rng = gi.rng_for(9)
+    Cv = gi.draw(rng, m * n, "u", dtype)
+    fn = pg.gemm_f32 if dtype == np.float32 else pg.gemm_f64
+    for (k, alpha, beta) in ((0, 1.0, 0.5), (16, 0.0, -2.0), (0, 1.0, 0.0), (16, 0.0, 1.0)):
+        dC = DevMat(gi.colmajor(Cv, m, n, ldc, gi.C_SENTINEL_F32 if dtype == np.float32
+                                else gi.C_SENTINEL_F64))
+        fn(m, n, k, alpha, None, m, None, max(k, 1), beta, dC.ptr, ldc)
+        got = logical(dC.storage(), m, n, ldc)
+        want = beta * logical(Cv.reshape(-1), m, n, m).astype(dtype) if beta != 0 else \
+            np.zeros((m, n), dtype)
+        assert np.array_equal(got, want.astype(dtype))
+        dC.assert_untouched_outside(m, n, ldc)
+
+
+def test_empty_shapes_touch_nothing():
+    dC = DevMat(np.ones(64, np.float32))
+    pg.gemm_f32(0, 8, 8, 1.0, None, 1, None, 8, 0.0, dC.ptr, 1)
+    pg.gemm_f32(8, 0, 8, 1.0, None, 8, None, 8, 0.0, dC.ptr, 8)
+    assert np.array_equal(dC.fetch().view(np.uint32), dC.host_before.view(np.uint32))
+
+
+def test_unaligned_pointer_takes_scalar_path():
+    p = gi.make_colmajor_problem("unal", np.float32, 260, 130, 96, 260, 96, 260, 0.75, -1.25,
+                                 seed=4, dist="n", c_dist="n")
+    C, _ = run_colmajor(p, offset=1)  # A's pointer is only 4-byte aligned
+    assert_f32_parity(C, oracle_full(p), p.k)
+
+
+def test_determinism_bitwise():
+    p = gi.workload("sgemm_2048")
+    C1, _ = run_colmajor(p)
+    C2, _ = run_colmajor(p)
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
+
+
+def test_linearity_bitwise():
+    p = gi.make_colmajor_problem("lin", np.float32, 1000, 700, 300, 1000, 300, 1000, 1.0,
+                                 0.0, seed=12, c_dist="u")
+    C1, _ = run_colmajor(p)
+    p.alpha, p.beta = 2.0, 0.5
+    C2, _ = run_colmajor(p)
+    C0 = logical(p.C, p.m, p.n, p.ldc)
+    want = (np.float32(2.0) * C1 + np.float32(0.5) * C0).astype(np.float32)
+    assert np.array_equal(C2.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_identity_and_closed_forms(dtype):
+    m, n = 1000, 300
+    eye = np.eye(m, dtype=dtype)
+    Bv = gi.draw(gi.rng_for(13), m * n, "u", dtype)
+    p = gi.Problem("eye", dtype, m, n, m, m, m, m, 1.0, 0.0,
+                   eye.T.ravel().copy(), Bv.copy(), np.full(m * n, np.nan, dtype))
+    C, _ = run_colmajor(p)
+    assert np.array_equal(C, Bv.reshape(n, m).T)
+    k = 5000
+    p = gi.Problem("ones", dtype, 96, 80, k, 96, k, 96, 1.0, 0.0,
+                   np.ones(96 * k, dtype), np.ones(k * 80, dtype), np.zeros(96 * 80, dtype))
+    C, _ = run_colmajor(p)
+    assert np.all(C == k)
+
+
+def test_python_gemm_layouts():
+    g = torch.Generator().manual_seed(0)
+    A = torch.rand(333, 200, generator=g, dtype=torch.float32) * 2 - 1
+    B = torch.rand(200, 150, generator=g, dtype=torch.float32) * 2 - 1
+    C0 = torch.rand(333, 150, generator=g, dtype=torch.float32) * 2 - 1
+    R = oracle.gemm(333, 150, 200, 0.5, A.t().contiguous().numpy().ravel(), 333,
+                    B.t().contiguous().numpy().ravel(), 200, 2.0,
+                    C0.t().contiguous().numpy().ravel(), 333)
+    # row-major (contiguous) tensors: operand swap
+    Cr = C0.clone().cuda()
+    pg.gemm(A.cuda(), B.cuda(), Cr, alpha=0.5, beta=2.0)
+    assert_f32_parity(Cr.cpu().numpy(), R, 200)
+    # column-major views with padding
+    Ap = torch.zeros(200, 340).cuda()   # storage of a 340-ld column-major A
+    Ap[:, :333] = A.t().cuda()
+    Acol = Ap.t()[:333, :]
+    Ccol_store = torch.zeros(150, 336).cuda()
+    Ccol_store[:, :333] = C0.t().cuda()
+    Ccol = Ccol_store.t()[:333, :]
+    Bcol = B.t().contiguous().cuda().t()
+    pg.gemm(Acol, Bcol, Ccol, alpha=0.5, beta=2.0)
+    assert_f32_parity(Ccol.cpu().numpy(), R, 200)
+    assert torch.all(Ccol_store[:, 333:] == 0)
