@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--secondary", nargs="*", default=["sgemm_2048"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run two device-to-device copies of this many MiB (a plain "
+                         "copy of known size, to scale HBM byte counters)")
     return ap.parse_args()
 
 
@@ -116,12 +119,52 @@ def time_workload(r: Resident, steps: int, warmup: int):
     return wall / steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms))
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "precision_gemm_02_amd", "csrc")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel sources and build script (identifies a build)."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "precision_gemm_02_amd", "build.py"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(variant: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counter runs, as recorded in
+    profiles/*counters*.md, or None if none matches this variant, workload
+    and the current kernel sources (the kernel changed since it was taken)."""
+    if not os.path.isdir(PROFILES):
+        return None
+    digest = kernel_source_digest()
+    for f in sorted(os.listdir(PROFILES)):
+        if "counters" not in f:
+            continue
+        kv = {}
+        for line in open(os.path.join(PROFILES, f)):
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                kv[k.strip("`")] = v.strip().strip("`")
+        if (kv.get("variant") == variant and kv.get("workload") == workload
+                and kv.get("source_digest") == digest and "traffic_bytes_per_launch" in kv):
+            return float(kv["traffic_bytes_per_launch"])
+    return None
+
+
 def roofline(r: Resident, kern_ms_mean: float):
     achieved = r.flops / (kern_ms_mean * 1e-3) / 1e12
     peak = PEAK_TFLOPS[r.dt]
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
-            "kernel": r.variant, "kernel_ms_mean": round(kern_ms_mean, 4)}
+            "frac": round(achieved / peak, 4),
+            "traffic": recorded_traffic(r.variant, r.name),
+            "algorithmic_bytes": r.algorithmic_bytes(),
+            "kernel": r.variant, "kernel_ms_mean": round(kern_ms_mean, 4),
+            "source_digest": kernel_source_digest()}
 
 
 def cpu_baseline(p, first_out: np.ndarray, seconds: float):
@@ -139,9 +182,9 @@ def cpu_baseline(p, first_out: np.ndarray, seconds: float):
                         dtype=p.dtype)
         return R, time.perf_counter() - t0
 
-    probe = min(p.n, 16)
+    probe = min(p.n, first_out.shape[1], 16)
     _, tp = run(probe)
-    cols = int(min(p.n, max(probe, probe * seconds / max(tp, 1e-6))))
+    cols = int(min(p.n, first_out.shape[1], max(probe, probe * seconds / max(tp, 1e-6))))
     R, dt = run(cols)
     flops = 2.0 * p.m * cols * p.k
     got = first_out[:, :cols].astype(np.float64)
@@ -178,8 +221,7 @@ def main():
     first_out = None
     if not args.no_cpu_baseline and not r.p.rowmajor:
         p = r.p
-        ncol = min(p.n, 4096)
-        first_out = r.C[: p.ldc * ncol].view(ncol, p.ldc)[:, : p.m].t().cpu().numpy()
+        first_out = r.C[: p.ldc * p.n].view(p.n, p.ldc)[:, : p.m].t().cpu().numpy()
     r.reset_c()
     ms_step, kern_mean, kern_med = time_workload(r, args.steps, args.warmup)
     value = r.flops / (ms_step * 1e-3) / 1e12
@@ -217,6 +259,15 @@ def main():
         r = r2
     if secondary:
         out["secondary"] = secondary
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = nbytes
+        del src, dst
     if first_out is not None:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(main_problem, first_out, args.cpu_seconds)
