@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstring>
+
 #include "pgemm.h"
 #include "variants.hpp"
 
@@ -52,11 +54,33 @@ bool vec_ok(const T* A, int lda, const T* B, int ldb, const T* C, int ldc) {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+template <typename T>
+int find_variant(const Variant<T>* table, int count, const char* name) {
+  for (int i = 0; i < count; ++i)
+    if (std::strcmp(table[i].name, name) == 0) return i;
+  return -1;
+}
+
+// Variant tables plus the indices the shape/alignment choice uses, looked up
+// by name once.
 struct Tables {
   const Variant<float>* f32;
   const Variant<double>* f64;
   int n32, n64;
-  Tables() { f32 = f32_variants(&n32); f64 = f64_variants(&n64); }
+  int f32_big_vec, f32_big_scalar, f32_small_vec, f32_small_scalar;
+  int f64_big_vec, f64_big_scalar, f64_small_vec, f64_small_scalar;
+  Tables() {
+    f32 = f32_variants(&n32);
+    f64 = f64_variants(&n64);
+    f32_big_vec = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_vec");
+    f32_big_scalar = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_scalar");
+    f32_small_vec = find_variant(f32, n32, "f32_128x128x16_w4x2_s4_vec");
+    f32_small_scalar = find_variant(f32, n32, "f32_128x128x16_w4x2_s4_scalar");
+    f64_big_vec = find_variant(f64, n64, "f64_256x128x16_w4x2_s3_vec");
+    f64_big_scalar = find_variant(f64, n64, "f64_256x128x16_w4x2_s3_scalar");
+    f64_small_vec = find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec");
+    f64_small_scalar = find_variant(f64, n64, "f64_128x128x16_w2x4_s3_scalar");
+  }
 };
 
 const Tables& tables() {
@@ -65,19 +89,22 @@ const Tables& tables() {
 }
 
 // Variant table index for fp32, by problem shape and alignment.
-//  * 256 x 256 tiles (wave tile 128 x 128) once they give at least one tile
-//    per compute unit: the most reuse per byte loaded.
+//  * 256 x 256 tiles once they give at least one tile per compute unit: the
+//    most reuse per byte loaded.
 //  * 128 x 128 tiles otherwise, so that e.g. 2048^2 still fills all 256 CUs.
 int choose_f32(int m, int n, bool vec) {
+  const Tables& t = tables();
   const long long t256 = ceil_div(m, 256) * ceil_div(n, 256);
-  const int big = 0, small = 4;  // rows of the fp32 table
-  return (t256 >= 256 ? big : small) + (vec ? 0 : 1);
+  if (t256 >= 256) return vec ? t.f32_big_vec : t.f32_big_scalar;
+  return vec ? t.f32_small_vec : t.f32_small_scalar;
 }
 
+// fp64: 256 x 128 tiles once they give a tile per compute unit, else 128^2.
 int choose_f64(int m, int n, bool vec) {
-  (void)m;
-  (void)n;
-  return vec ? 0 : 1;
+  const Tables& t = tables();
+  const long long tbig = ceil_div(m, 256) * ceil_div(n, 128);
+  if (tbig >= 256) return vec ? t.f64_big_vec : t.f64_big_scalar;
+  return vec ? t.f64_small_vec : t.f64_small_scalar;
 }
 
 template <typename T>

@@ -1,19 +1,28 @@
 // fp64 tile configurations (v_mfma_f64_16x16x4f64).
+//
+// Name: f64_<BM>x<BN>x<BK>_w<waves down>x<waves across>_s<LDS stages>_<vec|scalar>.
+// "vec" needs 16-byte aligned pointers and even leading dimensions.
 #include "variants.hpp"
 
 namespace pgemm {
 
-#define PGEMM_F64(BM, BN, BK, WM, WN, VEC, SUFFIX)                       \
-  {"f64_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_" #SUFFIX, BM, BN, BK, VEC, \
-   &launch_tile<TraitF64, BM, BN, BK, WM, WN, VEC>}
+#define PGEMM_F64(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                 \
+  {"f64_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, \
+   &launch_tile<TraitF64, BM, BN, BK, WM, WN, VEC, S>}
 
 // A host function owns the table so that it is never treated as device data.
 const Variant<double>* f64_variants(int* count) {
   static const Variant<double> table[] = {
-      PGEMM_F64(128, 128, 16, 2, 2, true, vec),   // wave tile 64 x 64
-      PGEMM_F64(128, 128, 16, 2, 2, false, scalar),
-      PGEMM_F64(128, 128, 32, 2, 2, true, vec),
-      PGEMM_F64(128, 128, 32, 2, 2, false, scalar),
+      // LDS ring of 3, 8 waves, wave tile 64 x 64: large problems
+      PGEMM_F64(256, 128, 16, 4, 2, 3, true, vec),
+      PGEMM_F64(256, 128, 16, 4, 2, 3, false, scalar),
+      // LDS ring of 3, 8 waves, wave tile 64 x 32: smaller problems
+      PGEMM_F64(128, 128, 16, 2, 4, 3, true, vec),
+      PGEMM_F64(128, 128, 16, 2, 4, 3, false, scalar),
+      // plain double buffering
+      PGEMM_F64(256, 128, 16, 2, 4, 2, true, vec),
+      PGEMM_F64(128, 128, 16, 2, 2, 2, true, vec),
+      PGEMM_F64(128, 128, 16, 2, 2, 2, false, scalar),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

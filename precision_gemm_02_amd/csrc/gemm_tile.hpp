@@ -134,7 +134,7 @@ __host__ __device__ inline int swz(int n) {
   }
 }
 
-template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES>
 struct TileCfg {
   using T = typename TR::T;
   static constexpr int NT = WGM * WGN * 64;           // threads per workgroup
@@ -148,13 +148,15 @@ struct TileCfg {
   static constexpr int A_STAGE = BK * BM, B_STAGE = BN * BK;  // elements
   static constexpr int A_CHUNKS = A_STAGE / V, B_CHUNKS = B_STAGE / V;
   static constexpr int A_LOADS = A_CHUNKS / NT, B_LOADS = B_CHUNKS / NT;
-  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE) * (int)sizeof(T);
+  static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * (int)sizeof(T);
   static_assert(WM * WGM == BM && WN * WGN == BN, "waves tile the block");
   static_assert(RB * TR::MB == WM && CB * TR::MB == WN, "blocks tile the wave");
   static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8, "row blocks");
   static_assert(BK % KG == 0, "K tile is whole groups");
   static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "even load split");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
+  static_assert(STAGES >= 2, "at least double buffering");
+  static_assert(STAGES == 2 || (BK / KG) % 2 == 0, "ring pipeline alternates two operand sets");
 };
 
 // ---------------------------------------------------------------- loads
@@ -187,10 +189,10 @@ __device__ __forceinline__ typename TR::chunk_t load_chunk_full(const typename T
 }
 
 // ---------------------------------------------------------------- kernel
-template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_tile_kernel(GemmArgs<typename TR::T> g) {
-  using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC>;
+  using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES>;
   using T = typename TR::T;
   using chunk_t = typename TR::chunk_t;
   using acc_t = typename TR::acc_t;
@@ -199,7 +201,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   constexpr int KG = Cfg::KG, KC = Cfg::KC;
   constexpr int A_LOADS = Cfg::A_LOADS, B_LOADS = Cfg::B_LOADS;
 
-  __shared__ __attribute__((aligned(16))) T lds[2 * (Cfg::A_STAGE + Cfg::B_STAGE)];
+  __shared__ __attribute__((aligned(16))) T lds[STAGES * (Cfg::A_STAGE + Cfg::B_STAGE)];
 
   int tm, tn;
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
@@ -215,41 +217,47 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   //  B: column q / KC, inner indices (q % KC)*V .. +V-1 of the tile.
   chunk_t ra[A_LOADS], rb[B_LOADS];
 
-  auto gload = [&](int kt) {
+  // Whole tile in range: unmasked loads, no branches.
+  auto gload_full = [&](int kt) {
     const int k0 = kt * BK;
-    if (full_mn && k0 + BK <= K) {
 #pragma unroll
-      for (int i = 0; i < A_LOADS; ++i) {
-        const int q = tid + i * NT;
-        const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
-        ra[i] = load_chunk_full<TR, VEC>(g.A + (size_t)(k0 + kk) * lda + (m0 + mm));
-      }
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) {
-        const int q = tid + i * NT;
-        const int nn = q / KC, kk = (q % KC) * V;
-        rb[i] = load_chunk_full<TR, VEC>(g.B + (size_t)(n0 + nn) * ldb + (k0 + kk));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < A_LOADS; ++i) {
-        const int q = tid + i * NT;
-        const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
-        const int k = k0 + kk, m = m0 + mm;
-        const int valid = (k < K) ? min(M - m, V) : 0;
-        if (valid > 0) ra[i] = load_chunk<TR, VEC>(g.A + (size_t)k * lda + m, valid);
-        else ra[i] = chunk_t{};
-      }
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) {
-        const int q = tid + i * NT;
-        const int nn = q / KC, kk = (q % KC) * V;
-        const int n = n0 + nn, k = k0 + kk;
-        const int valid = (n < N) ? min(K - k, V) : 0;
-        if (valid > 0) rb[i] = load_chunk<TR, VEC>(g.B + (size_t)n * ldb + k, valid);
-        else rb[i] = chunk_t{};
-      }
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int q = tid + i * NT;
+      const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
+      ra[i] = load_chunk_full<TR, VEC>(g.A + (size_t)(k0 + kk) * lda + (m0 + mm));
     }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int q = tid + i * NT;
+      const int nn = q / KC, kk = (q % KC) * V;
+      rb[i] = load_chunk_full<TR, VEC>(g.B + (size_t)(n0 + nn) * ldb + (k0 + kk));
+    }
+  };
+  // Edge tiles and the K tail: out-of-range elements load as zero.
+  auto gload_masked = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int q = tid + i * NT;
+      const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
+      const int k = k0 + kk, m = m0 + mm;
+      const int valid = (k < K) ? min(M - m, V) : 0;
+      if (valid > 0) ra[i] = load_chunk<TR, VEC>(g.A + (size_t)k * lda + m, valid);
+      else ra[i] = chunk_t{};
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int q = tid + i * NT;
+      const int nn = q / KC, kk = (q % KC) * V;
+      const int n = n0 + nn, k = k0 + kk;
+      const int valid = (n < N) ? min(K - k, V) : 0;
+      if (valid > 0) rb[i] = load_chunk<TR, VEC>(g.B + (size_t)n * ldb + k, valid);
+      else rb[i] = chunk_t{};
+    }
+  };
+  auto gload = [&](int kt) {
+    if (full_mn && (kt + 1) * BK <= K) gload_full(kt);
+    else gload_masked(kt);
   };
 
   auto lstore = [&](int stage) {
@@ -279,57 +287,188 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   const int lrow = lane % MB;   // block row (A) / block column (B) of this lane
   const int kslot = lane / MB;  // which inner-index slot of the instruction
 
-  auto compute = [&](int stage) {
+  // Operands of one group of KG inner indices: CB chunks of B (V inner
+  // indices each) and, for each of the V steps, the RB row values of A.
+  struct GroupOps {
+    chunk_t b[CB];
+    T a[V][RB];
+  };
+  auto read_ops = [&](int stage, int kg, GroupOps& o) {
     const T* As = lds + stage * (Cfg::A_STAGE + Cfg::B_STAGE);
     const T* Bs = As + Cfg::A_STAGE;
 #pragma unroll
-    for (int kg = 0; kg < BK; kg += KG) {
-      // B: one 16-byte read per column block gives V consecutive k.
-      chunk_t bv[CB];
+    for (int c = 0; c < CB; ++c) {
+      const int n = wcol + c * MB + lrow;
+      const int kc = kg / V + kslot;
+      o.b[c] = *reinterpret_cast<const chunk_t*>(Bs + n * BK + ((kc ^ swz<KC>(n)) * V));
+    }
 #pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const int n = wcol + c * MB + lrow;
-        const int kc = kg / V + kslot;
-        bv[c] = *reinterpret_cast<const chunk_t*>(Bs + n * BK + ((kc ^ swz<KC>(n)) * V));
-      }
+    for (int s = 0; s < V; ++s) {
+      const int k = kg + V * kslot + s;
 #pragma unroll
-      for (int s = 0; s < V; ++s) {
-        const int k = kg + V * kslot + s;
-        T av[RB];
+      for (int sb = 0; sb < SB; ++sb) {
+        const T* p = As + k * BM + wrow + sb * MB * W + W * lrow;
+        if constexpr (W == 4) {
+          floatx4 t = *reinterpret_cast<const floatx4*>(p);
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-          const T* p = As + k * BM + wrow + sb * MB * W + W * lrow;
-          if constexpr (W == 4) {
-            floatx4 t = *reinterpret_cast<const floatx4*>(p);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) av[sb * W + e] = t[e];
-          } else if constexpr (W == 2) {
-            typedef T T2 __attribute__((ext_vector_type(2)));
-            T2 t = *reinterpret_cast<const T2*>(p);
-            av[sb * W + 0] = t[0];
-            av[sb * W + 1] = t[1];
-          } else {
-            av[sb] = p[0];
-          }
+          for (int e = 0; e < 4; ++e) o.a[s][sb * W + e] = t[e];
+        } else if constexpr (W == 2) {
+          typedef T T2 __attribute__((ext_vector_type(2)));
+          T2 t = *reinterpret_cast<const T2*>(p);
+          o.a[s][sb * W + 0] = t[0];
+          o.a[s][sb * W + 1] = t[1];
+        } else {
+          o.a[s][sb] = p[0];
         }
-#pragma unroll
-        for (int b = 0; b < RB; ++b)
-#pragma unroll
-          for (int c = 0; c < CB; ++c) acc[b][c] = TR::mfma(av[b], bv[c][s], acc[b][c]);
       }
     }
   };
+  auto mma = [&](const GroupOps& o) {
+#pragma unroll
+    for (int s = 0; s < V; ++s)
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) acc[b][c] = TR::mfma(o.a[s][b], o.b[c][s], acc[b][c]);
+  };
 
+  constexpr int NG = BK / KG;
   const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    compute(kt & 1);
-    if (more) lstore((kt + 1) & 1);
+
+  if constexpr (STAGES == 2) {
+    // Two LDS stages.  Tile t+1 is fetched from HBM into registers while
+    // tile t feeds the MFMAs, then written to the other stage; one barrier
+    // per tile.  With one wave per SIMD (256 threads) the operands of group
+    // g+1 are read into a second register set before the MFMAs of group g,
+    // so LDS latency hides behind the same wave's matrix-core work; with more
+    // waves per SIMD the other waves fill those gaps and one set is used.
+    constexpr bool PIPE_OPS = NT <= 256;
+    auto compute = [&](int stage) {
+      if constexpr (PIPE_OPS) {
+        GroupOps ops[2];
+        read_ops(stage, 0, ops[0]);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          if (gi + 1 < NG) read_ops(stage, (gi + 1) * KG, ops[(gi + 1) & 1]);
+          // keep the reads above the MFMAs (the scheduler would otherwise
+          // sink each read next to its first use and wait for it there)
+          __builtin_amdgcn_sched_barrier(0);
+          mma(ops[gi & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          GroupOps ops;
+          read_ops(stage, gi * KG, ops);
+          mma(ops);
+        }
+      }
+    };
+    gload(0);
+    lstore(0);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) gload(kt + 1);
+      compute(kt & 1);
+      if (more) lstore((kt + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    // Ring of S = STAGES LDS stages, one barrier per tile.  At the top of
+    // iteration kt the registers hold tile kt+S-1 (fetched one iteration
+    // earlier, so HBM latency has a whole tile of MFMA work to hide behind);
+    // they are written to stage (kt+S-1)%S, which last held tile kt-1 and was
+    // released by the previous barrier, and tile kt+S is fetched.  The last
+    // group of tile kt prefetches the operands of group 0 of tile kt+1, which
+    // was written S-2 >= 1 barriers earlier, so the MFMAs of the next tile
+    // start right after the barrier without waiting for LDS.
+    constexpr int S = STAGES;
+    for (int t = 0; t < S - 1; ++t)
+      if (t < nk) {
+        gload(t);
+        lstore(t);
+      }
+    if (S - 1 < nk) gload(S - 1);
+    __syncthreads();
+    GroupOps ops[2];
+    read_ops(0, 0, ops[0]);
+    // Drain those reads so that both edges into the loop header carry no
+    // LDS operations in flight: otherwise the compiler's wait-count
+    // insertion has to assume the prologue's reads are pending at every
+    // iteration and makes the first MFMAs wait for the tile's LDS stores.
+    // (s_waitcnt lgkmcnt(0); the vector-memory and export counts at their
+    // no-wait maxima.)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    // Instruction counts of one iteration, for the interleave below.
+    constexpr int N_WR = A_LOADS + B_LOADS;                        // ds_write
+    constexpr int N_LD = (A_LOADS + B_LOADS) * (VEC ? 1 : V);      // global loads
+    constexpr int MPG = V * RB * CB;                                // MFMAs per group
+    constexpr bool INTERLEAVE = NG >= 2 && MPG >= N_WR + N_LD;
+    int st = 0;                       // stage of tile kt
+    int kt = 0;
+    // Steady state, while tile kt+S exists and is whole (and the tile is
+    // inside C): one branch-free block per iteration.  With in-order issue,
+    // the tile's LDS stores and global loads are slotted one by one between
+    // group 0's MFMAs (each executes while an MFMA occupies the matrix core)
+    // instead of running as a block while the matrix core idles.
+    const int nk_fast = (INTERLEAVE && full_mn) ? max(0, K / BK - S) : 0;
+    for (; kt < nk_fast; ++kt) {
+      const int st_next = (st + 1 == S) ? 0 : st + 1;
+      const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
+      read_ops(st, KG, ops[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      lstore(st_store);
+      gload_full(kt + S);
+      mma(ops[0]);
+      if constexpr (INTERLEAVE) {
+#pragma unroll
+        for (int i = 0; i < N_WR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        }
+#pragma unroll
+        for (int i = 0; i < N_LD; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MPG - N_WR - N_LD, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int gi = 1; gi < NG; ++gi) {
+        // the next tile (kt+1 < nk_fast + S <= nk) always exists here
+        if (gi + 1 < NG) read_ops(st, (gi + 1) * KG, ops[(gi + 1) & 1]);
+        else read_ops(st_next, 0, ops[(gi + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(ops[gi & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      st = st_next;
+    }
+    // Remaining iterations (edge tiles, the K tail, the last S tiles).
+    for (; kt < nk; ++kt) {
+      const int st_next = (st + 1 == S) ? 0 : st + 1;
+      const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
+      // At the last tile the prefetch re-reads this tile's own stage (in
+      // bounds, unused): a branch here would make the compiler wait for the
+      // prefetch before the current group's MFMAs.
+      const int st_pf = (kt + 1 < nk) ? st_next : st;
+      if (kt + S - 1 < nk) lstore(st_store);
+      if (kt + S < nk) gload(kt + S);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        if (gi + 1 < NG) read_ops(st, (gi + 1) * KG, ops[(gi + 1) & 1]);
+        else read_ops(st_pf, 0, ops[(gi + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(ops[gi & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      st = st_next;
+    }
   }
 
   // Epilogue.  A lane's accumulator registers come in runs of RUN_R
@@ -342,47 +481,69 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   constexpr int RUN = TR::RUN_R * W;
   constexpr int NRUN = TR::NACC / TR::RUN_R;
   constexpr bool VEC_C = VEC && (RUN % V == 0);
+  const bool read_c = beta != T(0);
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
     const int col = n0 + wcol + c * MB + lrow;
+    T* pcol = g.C + (size_t)col * ldc;
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
+      const int row0 = m0 + wrow + sb * MB * W;
+      if (full_mn) {
+        // Whole tile in range: issue every C load of this column block
+        // first, then the multiply-adds and stores, so that the loads'
+        // latency is paid once rather than once per run.
+        T cv[NRUN][RUN];
+        if (read_c) {
 #pragma unroll
-      for (int run = 0; run < NRUN; ++run) {
-        const int row = m0 + wrow + sb * MB * W + W * TR::irow(run, kslot);
-        T out[RUN];
+          for (int run = 0; run < NRUN; ++run) {
+            const T* pc = pcol + row0 + W * TR::irow(run, kslot);
+            if constexpr (VEC_C) {
 #pragma unroll
-        for (int o = 0; o < RUN; ++o)
-          out[o] = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
-        T* pc = g.C + (size_t)col * ldc + row;
-        if (full_mn || (col < N && row + RUN <= M)) {
+              for (int h = 0; h < RUN / V; ++h) {
+                chunk_t v = *reinterpret_cast<const chunk_t*>(pc + h * V);
+#pragma unroll
+                for (int e = 0; e < V; ++e) cv[run][h * V + e] = v[e];
+              }
+            } else {
+#pragma unroll
+              for (int o = 0; o < RUN; ++o) cv[run][o] = pc[o];
+            }
+          }
+        }
+#pragma unroll
+        for (int run = 0; run < NRUN; ++run) {
+          T* pc = pcol + row0 + W * TR::irow(run, kslot);
+          T out[RUN];
+#pragma unroll
+          for (int o = 0; o < RUN; ++o) {
+            out[o] = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+            if (read_c) out[o] = __builtin_fma(beta, cv[run][o], out[o]);
+          }
           if constexpr (VEC_C) {
 #pragma unroll
             for (int h = 0; h < RUN / V; ++h) {
               chunk_t v;
 #pragma unroll
               for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
-              if (beta != T(0)) {
-                chunk_t cv = *reinterpret_cast<const chunk_t*>(pc + h * V);
-#pragma unroll
-                for (int e = 0; e < V; ++e) v[e] = __builtin_fma(beta, cv[e], v[e]);
-              }
               *reinterpret_cast<chunk_t*>(pc + h * V) = v;
             }
           } else {
 #pragma unroll
-            for (int o = 0; o < RUN; ++o) {
-              T v = out[o];
-              if (beta != T(0)) v = __builtin_fma(beta, pc[o], v);
-              pc[o] = v;
-            }
+            for (int o = 0; o < RUN; ++o) pc[o] = out[o];
           }
-        } else if (col < N) {
+        }
+      } else if (col < N) {
+        // Edge tile: element-wise bounds checks.
+#pragma unroll
+        for (int run = 0; run < NRUN; ++run) {
+          const int row = row0 + W * TR::irow(run, kslot);
+          T* pc = pcol + row;
 #pragma unroll
           for (int o = 0; o < RUN; ++o) {
             if (row + o < M) {
-              T v = out[o];
-              if (beta != T(0)) v = __builtin_fma(beta, pc[o], v);
+              T v = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+              if (read_c) v = __builtin_fma(beta, pc[o], v);
               pc[o] = v;
             }
           }

@@ -19,7 +19,7 @@ struct Variant {
 };
 
 // Launch one tile configuration: one workgroup per BM x BN tile of C.
-template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES>
 hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
   using T = typename TR::T;
   GemmArgs<T> g = a;
@@ -29,7 +29,7 @@ hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
   void* args[] = {&g};
   const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(WGM * WGN * 64);
   return hipLaunchKernel(reinterpret_cast<const void*>(
-                             &gemm_tile_kernel<TR, BM, BN, BK, WGM, WGN, VEC>),
+                             &gemm_tile_kernel<TR, BM, BN, BK, WGM, WGN, VEC, STAGES>),
                          grid, block, args, 0, stream);
 }
 
