@@ -52,17 +52,19 @@ extern "C" {
  *   C: ldc >= max(1, m)                (arguments 10, 11)
  *   A, B may be NULL only if k == 0 or alpha == 0; C only if m == 0 or n == 0.
  *
- * Any leading dimension and any 4-byte-aligned pointer is accepted; 16-byte
- * alignment of a pointer with a leading dimension that is a multiple of 4
- * selects the 128-bit load path.
+ * Any leading dimension and any 4-byte-aligned pointer is accepted.  Global
+ * memory is moved in 16-byte accesses either way (gfx950 needs only dword
+ * alignment for them); 16-byte aligned pointers with leading dimensions that
+ * are multiples of 4 select kernels that also assume that alignment.
  */
 int gemm_f32(int m, int n, int k, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc,
              void *stream);
 
 /*
- * Double precision, same contract as gemm_f32 with 8-byte elements (the
- * 128-bit path needs 16-byte pointers and even leading dimensions).
+ * Double precision, same contract as gemm_f32 with 8-byte elements
+ * (pointers 8-byte aligned; the aligned kernels need 16-byte pointers and
+ * even leading dimensions).
  */
 int gemm_f64(int m, int n, int k, double alpha, const double *A, int lda,
              const double *B, int ldb, double beta, double *C, int ldc,

@@ -54,11 +54,13 @@ bool vec_ok(const T* A, int lda, const T* B, int ldb, const T* C, int ldc) {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+// Index of the named variant; the first entry if the name is not compiled in
+// (the host tests check that every name the choice uses exists).
 template <typename T>
 int find_variant(const Variant<T>* table, int count, const char* name) {
   for (int i = 0; i < count; ++i)
     if (std::strcmp(table[i].name, name) == 0) return i;
-  return -1;
+  return 0;
 }
 
 // Variant tables plus the indices the shape/alignment choice uses, looked up
@@ -67,19 +69,19 @@ struct Tables {
   const Variant<float>* f32;
   const Variant<double>* f64;
   int n32, n64;
-  int f32_big_vec, f32_big_scalar, f32_small_vec, f32_small_scalar;
-  int f64_big_vec, f64_big_scalar, f64_small_vec, f64_small_scalar;
+  int f32_big_vec, f32_big_ua, f32_small_vec, f32_small_ua;
+  int f64_big_vec, f64_big_ua, f64_small_vec, f64_small_ua;
   Tables() {
     f32 = f32_variants(&n32);
     f64 = f64_variants(&n64);
     f32_big_vec = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_vec");
-    f32_big_scalar = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_scalar");
-    f32_small_vec = find_variant(f32, n32, "f32_128x128x16_w4x2_s4_vec");
-    f32_small_scalar = find_variant(f32, n32, "f32_128x128x16_w4x2_s4_scalar");
+    f32_big_ua = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_ua");
+    f32_small_vec = find_variant(f32, n32, "f32_128x128x32_w4x2_s3_vec");
+    f32_small_ua = find_variant(f32, n32, "f32_128x128x32_w4x2_s3_ua");
     f64_big_vec = find_variant(f64, n64, "f64_256x128x16_w4x2_s3_vec");
-    f64_big_scalar = find_variant(f64, n64, "f64_256x128x16_w4x2_s3_scalar");
+    f64_big_ua = find_variant(f64, n64, "f64_256x128x16_w4x2_s3_ua");
     f64_small_vec = find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec");
-    f64_small_scalar = find_variant(f64, n64, "f64_128x128x16_w2x4_s3_scalar");
+    f64_small_ua = find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua");
   }
 };
 
@@ -95,16 +97,16 @@ const Tables& tables() {
 int choose_f32(int m, int n, bool vec) {
   const Tables& t = tables();
   const long long t256 = ceil_div(m, 256) * ceil_div(n, 256);
-  if (t256 >= 256) return vec ? t.f32_big_vec : t.f32_big_scalar;
-  return vec ? t.f32_small_vec : t.f32_small_scalar;
+  if (t256 >= 256) return vec ? t.f32_big_vec : t.f32_big_ua;
+  return vec ? t.f32_small_vec : t.f32_small_ua;
 }
 
 // fp64: 256 x 128 tiles once they give a tile per compute unit, else 128^2.
 int choose_f64(int m, int n, bool vec) {
   const Tables& t = tables();
   const long long tbig = ceil_div(m, 256) * ceil_div(n, 128);
-  if (tbig >= 256) return vec ? t.f64_big_vec : t.f64_big_scalar;
-  return vec ? t.f64_small_vec : t.f64_small_scalar;
+  if (tbig >= 256) return vec ? t.f64_big_vec : t.f64_big_ua;
+  return vec ? t.f64_small_vec : t.f64_small_ua;
 }
 
 template <typename T>

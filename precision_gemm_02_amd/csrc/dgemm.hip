@@ -1,7 +1,9 @@
 // fp64 tile configurations (v_mfma_f64_16x16x4f64).
 //
-// Name: f64_<BM>x<BN>x<BK>_w<waves down>x<waves across>_s<LDS stages>_<vec|scalar>.
-// "vec" needs 16-byte aligned pointers and even leading dimensions.
+// Name: f64_<BM>x<BN>x<BK>_w<waves down>x<waves across>_s<LDS stages>_<vec|ua>.
+// "vec" needs 16-byte aligned pointers and even leading dimensions; "ua"
+// (unaligned) takes any element-aligned input and still moves 16 bytes per
+// global access.
 #include "variants.hpp"
 
 namespace pgemm {
@@ -15,14 +17,14 @@ const Variant<double>* f64_variants(int* count) {
   static const Variant<double> table[] = {
       // LDS ring of 3, 8 waves, wave tile 64 x 64: large problems
       PGEMM_F64(256, 128, 16, 4, 2, 3, true, vec),
-      PGEMM_F64(256, 128, 16, 4, 2, 3, false, scalar),
+      PGEMM_F64(256, 128, 16, 4, 2, 3, false, ua),
       // LDS ring of 3, 8 waves, wave tile 64 x 32: smaller problems
       PGEMM_F64(128, 128, 16, 2, 4, 3, true, vec),
-      PGEMM_F64(128, 128, 16, 2, 4, 3, false, scalar),
+      PGEMM_F64(128, 128, 16, 2, 4, 3, false, ua),
       // plain double buffering
       PGEMM_F64(256, 128, 16, 2, 4, 2, true, vec),
       PGEMM_F64(128, 128, 16, 2, 2, 2, true, vec),
-      PGEMM_F64(128, 128, 16, 2, 2, 2, false, scalar),
+      PGEMM_F64(128, 128, 16, 2, 2, 2, false, ua),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

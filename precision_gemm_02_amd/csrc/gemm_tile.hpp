@@ -160,30 +160,43 @@ struct TileCfg {
 };
 
 // ---------------------------------------------------------------- loads
-// One 16-byte chunk of V consecutive elements starting at p; element e is
-// in range when e < valid.  valid >= V uses one vector load (VEC) or V
-// scalar loads; out-of-range elements are zero and are never read.
-template <class TR, bool VEC>
-__device__ __forceinline__ typename TR::chunk_t load_chunk(const typename TR::T* p, int valid) {
-  using T = typename TR::T;
-  typename TR::chunk_t v;
-  if (VEC && valid >= TR::V) {
-    v = *reinterpret_cast<const typename TR::chunk_t*>(p);
-  } else {
-#pragma unroll
-    for (int e = 0; e < TR::V; ++e) v[e] = (e < valid) ? p[e] : T(0);
-  }
-  return v;
-}
-
+// 16 bytes at p.  VEC: p is 16-byte aligned.  Otherwise p is only element
+// aligned; multi-dword global accesses on gfx950 need dword alignment only,
+// so a byte copy of 16 bytes still becomes one global_load_dwordx4 (and one
+// global_store_dwordx4 for stores).
 template <class TR, bool VEC>
 __device__ __forceinline__ typename TR::chunk_t load_chunk_full(const typename TR::T* p) {
   typename TR::chunk_t v;
   if constexpr (VEC) {
     v = *reinterpret_cast<const typename TR::chunk_t*>(p);
   } else {
+    __builtin_memcpy(&v, p, sizeof(v));
+  }
+  return v;
+}
+
+template <class TR, bool VEC>
+__device__ __forceinline__ void store_chunk(typename TR::T* p, typename TR::chunk_t v) {
+  if constexpr (VEC) {
+    *reinterpret_cast<typename TR::chunk_t*>(p) = v;
+  } else {
+    __builtin_memcpy(p, &v, sizeof(v));
+  }
+}
+
+// One chunk of V consecutive elements starting at p; element e is in range
+// when e < valid.  A whole chunk uses one 16-byte load; a partial chunk loads
+// its in-range elements one by one; out-of-range elements are zero and are
+// never read.
+template <class TR, bool VEC>
+__device__ __forceinline__ typename TR::chunk_t load_chunk(const typename TR::T* p, int valid) {
+  using T = typename TR::T;
+  typename TR::chunk_t v;
+  if (valid >= TR::V) {
+    v = load_chunk_full<TR, VEC>(p);
+  } else {
 #pragma unroll
-    for (int e = 0; e < TR::V; ++e) v[e] = p[e];
+    for (int e = 0; e < TR::V; ++e) v[e] = (e < valid) ? p[e] : T(0);
   }
   return v;
 }
@@ -403,7 +416,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     // Instruction counts of one iteration, for the interleave below.
     constexpr int N_WR = A_LOADS + B_LOADS;                        // ds_write
-    constexpr int N_LD = (A_LOADS + B_LOADS) * (VEC ? 1 : V);      // global loads
+    constexpr int N_LD = A_LOADS + B_LOADS;                        // global loads
     constexpr int MPG = V * RB * CB;                                // MFMAs per group
     constexpr bool INTERLEAVE = NG >= 2 && MPG >= N_WR + N_LD;
     int st = 0;                       // stage of tile kt
@@ -480,7 +493,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   const int ldc = g.ldc;
   constexpr int RUN = TR::RUN_R * W;
   constexpr int NRUN = TR::NACC / TR::RUN_R;
-  constexpr bool VEC_C = VEC && (RUN % V == 0);
+  constexpr bool VEC_C = (RUN % V == 0);   // whole 16-byte chunks per run
   const bool read_c = beta != T(0);
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
@@ -501,7 +514,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
             if constexpr (VEC_C) {
 #pragma unroll
               for (int h = 0; h < RUN / V; ++h) {
-                chunk_t v = *reinterpret_cast<const chunk_t*>(pc + h * V);
+                chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
 #pragma unroll
                 for (int e = 0; e < V; ++e) cv[run][h * V + e] = v[e];
               }
@@ -526,7 +539,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
               chunk_t v;
 #pragma unroll
               for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
-              *reinterpret_cast<chunk_t*>(pc + h * V) = v;
+              store_chunk<TR, VEC>(pc + h * V, v);
             }
           } else {
 #pragma unroll

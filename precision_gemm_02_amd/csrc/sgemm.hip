@@ -1,8 +1,9 @@
 // fp32 tile configurations (v_mfma_f32_32x32x2f32).
 //
-// Name: f32_<BM>x<BN>x<BK>_w<waves down>x<waves across>_s<LDS stages>_<vec|scalar>.
+// Name: f32_<BM>x<BN>x<BK>_w<waves down>x<waves across>_s<LDS stages>_<vec|ua>.
 // "vec" needs 16-byte aligned pointers and leading dimensions that are
-// multiples of 4; "scalar" takes any element-aligned input.
+// multiples of 4; "ua" (unaligned) takes any element-aligned input and still
+// moves 16 bytes per global access.
 #include "variants.hpp"
 
 namespace pgemm {
@@ -16,19 +17,20 @@ const Variant<float>* f32_variants(int* count) {
   static const Variant<float> table[] = {
       // LDS ring of 3, 8 waves (2 per SIMD), wave tile 128 x 64: large problems
       PGEMM_F32(256, 256, 16, 2, 4, 3, true, vec),
-      PGEMM_F32(256, 256, 16, 2, 4, 3, false, scalar),
-      // LDS ring of 4, 8 waves, wave tile 32 x 64: fills 256 CUs from 2048^2
-      PGEMM_F32(128, 128, 16, 4, 2, 4, true, vec),
-      PGEMM_F32(128, 128, 16, 4, 2, 4, false, scalar),
+      PGEMM_F32(256, 256, 16, 2, 4, 3, false, ua),
+      // LDS ring of 3, 8 waves, wave tile 32 x 64: fills 256 CUs from 2048^2
+      PGEMM_F32(128, 128, 32, 4, 2, 3, true, vec),
+      PGEMM_F32(128, 128, 32, 4, 2, 3, false, ua),
+      PGEMM_F32(128, 128, 16, 4, 2, 4, true, vec),     // ring of 4, BK 16
+      PGEMM_F32(128, 128, 16, 4, 2, 4, false, ua),
       // ring, 4 waves (1 per SIMD)
       PGEMM_F32(256, 256, 16, 2, 2, 3, true, vec),     // wave tile 128 x 128
       PGEMM_F32(128, 128, 16, 2, 2, 4, true, vec),     // wave tile 64 x 64
-      PGEMM_F32(128, 128, 32, 4, 2, 3, true, vec),
       // plain double buffering (two LDS stages), 4 waves
       PGEMM_F32(256, 256, 32, 2, 2, 2, true, vec),
-      PGEMM_F32(256, 256, 32, 2, 2, 2, false, scalar),
+      PGEMM_F32(256, 256, 32, 2, 2, 2, false, ua),
       PGEMM_F32(128, 128, 32, 2, 2, 2, true, vec),
-      PGEMM_F32(128, 128, 32, 2, 2, 2, false, scalar),
+      PGEMM_F32(128, 128, 32, 2, 2, 2, false, ua),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

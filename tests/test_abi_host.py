@@ -125,16 +125,16 @@ def test_selection_by_shape_and_alignment():
     assert name_of(v).startswith("f32_256x256") and name_of(v).endswith("_vec")
     v = pg.select_f32(2048, 2048, 2048, 1.0, FAKE, 2048, FAKE, 2048, 0.0, FAKE, 2048)
     assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_vec")
-    # odd leading dimensions force the scalar path
+    # odd leading dimensions select the unaligned path
     v = pg.select_f32(4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
-    assert name_of(v).endswith("_scalar")
-    # a 4-byte aligned pointer forces the scalar path
+    assert name_of(v).endswith("_ua")
+    # a 4-byte aligned pointer selects the unaligned path
     v = pg.select_f32(512, 512, 512, 1.0, FAKE_ODD, 512, FAKE, 512, 0.0, FAKE, 512)
-    assert name_of(v).endswith("_scalar")
+    assert name_of(v).endswith("_ua")
     v = pg.select_f64(4096, 4096, 4096, 1.0, FAKE, 4104, FAKE, 4104, 1.0, FAKE, 4104)
     assert name_of(v).startswith("f64_") and name_of(v).endswith("_vec")
     v = pg.select_f64(100, 100, 100, 1.0, FAKE, 101, FAKE, 100, 1.0, FAKE, 100)
-    assert name_of(v).endswith("_scalar")
+    assert name_of(v).endswith("_ua")
 
 
 def test_status_strings():

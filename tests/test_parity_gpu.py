@@ -15,6 +15,7 @@ Bars:
     must be bit-identical after the call; A/B padding is NaN.
 """
 import os
+import re
 import sys
 
 import numpy as np
@@ -156,7 +157,7 @@ def variant_ids(prefix):
 
 
 def leading_dims(m, k, vec, chunk, t):
-    """Vector variants: multiples of the 16-byte chunk; scalar: odd values."""
+    """Aligned ("vec") variants: multiples of the 16-byte chunk; unaligned: odd."""
     if vec:
         up = lambda x: -(-x // chunk) * chunk  # noqa: E731
         extra = chunk * (t % 2)
@@ -178,6 +179,42 @@ def test_every_variant_exact_integer(variant):
         say(name, (m, n, k), (alpha, beta), "ld", lds)
         C, _ = run_colmajor(p, variant=variant)
         assert_bitwise(C, oracle_full(p))
+
+
+def ring_variants():
+    out = []
+    for v, n in pg.variants().items():
+        m = re.match(r"f(32|64)_(\d+)x(\d+)x(\d+)_w\d+x\d+_s(\d+)_(vec|ua)$", n)
+        if m and int(m.group(5)) > 2:
+            out.append(v)
+    return out
+
+
+@pytest.mark.parametrize("variant", ring_variants(), ids=lambda v: pg.variants()[v])
+def test_ring_pipeline_boundaries(variant):
+    """K around the start and end of the branch-free steady-state loop
+    (which runs while tile kt+S is whole), and tiles partly outside C."""
+    name = pg.variants()[variant]
+    m = re.match(r"f(32|64)_(\d+)x(\d+)x(\d+)_w\d+x\d+_s(\d+)_(vec|ua)$", name)
+    prec, BM, BN, BK, S, kind = m.group(1), int(m.group(2)), int(m.group(3)), \
+        int(m.group(4)), int(m.group(5)), m.group(6)
+    dtype = np.float32 if prec == "32" else np.float64
+    chunk = 4 if dtype == np.float32 else 2
+    Ks = sorted({1, BK - 1, BK * (S - 1), BK * S, BK * S + 1, BK * (S + 1) - 1,
+                 BK * (S + 1), BK * (S + 1) + 1, BK * (S + 2) + 3, BK * (2 * S + 3)})
+    shapes = [(2 * BM, 2 * BN), (2 * BM + 5, BN + 3)]
+    t = 0
+    for (mm, nn) in shapes:
+        for k in Ks:
+            if k <= 0:
+                continue
+            lds = leading_dims(mm, k, kind == "vec", chunk, t)
+            alpha, beta = ALPHA_BETA[t % len(ALPHA_BETA)]
+            p = exact_problem(dtype, mm, nn, k, alpha, beta, lds, seed=200 + t)
+            say(name, (mm, nn, k), (alpha, beta), "ld", lds)
+            C, _ = run_colmajor(p, variant=variant)
+            assert_bitwise(C, oracle_full(p))
+            t += 1
 
 
 @pytest.mark.parametrize("name", ["sgemm_128", "sgemm_2048", "sgemm_sweep_4096",
@@ -246,7 +283,7 @@ def test_empty_shapes_touch_nothing():
     assert np.array_equal(dC.fetch().view(np.uint32), dC.host_before.view(np.uint32))
 
 
-def test_unaligned_pointer_takes_scalar_path():
+def test_unaligned_pointer_takes_unaligned_path():
     p = gi.make_colmajor_problem("unal", np.float32, 260, 130, 96, 260, 96, 260, 0.75, -1.25,
                                  seed=4, dist="n", c_dist="n")
     C, _ = run_colmajor(p, offset=1)  # A's pointer is only 4-byte aligned
