@@ -76,8 +76,8 @@ struct Tables {
     f64 = f64_variants(&n64);
     f32_big_vec = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_vec");
     f32_big_ua = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_ua");
-    f32_small_vec = find_variant(f32, n32, "f32_128x128x32_w4x2_s3_vec");
-    f32_small_ua = find_variant(f32, n32, "f32_128x128x32_w4x2_s3_ua");
+    f32_small_vec = find_variant(f32, n32, "f32_128x128x32_w2x2_s3_k2_vec");
+    f32_small_ua = find_variant(f32, n32, "f32_128x128x32_w2x2_s3_k2_ua");
     f64_big_vec = find_variant(f64, n64, "f64_256x128x16_w4x2_s3_vec");
     f64_big_ua = find_variant(f64, n64, "f64_256x128x16_w4x2_s3_ua");
     f64_small_vec = find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec");

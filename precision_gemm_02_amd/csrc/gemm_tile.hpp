@@ -134,10 +134,10 @@ __host__ __device__ inline int swz(int n) {
   }
 }
 
-template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES>
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS>
 struct TileCfg {
   using T = typename TR::T;
-  static constexpr int NT = WGM * WGN * 64;           // threads per workgroup
+  static constexpr int NT = WGM * WGN * 64 * KS;      // threads per workgroup
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
   static constexpr int RB = WM / TR::MB, CB = WN / TR::MB;
   static constexpr int V = TR::V;
@@ -156,7 +156,12 @@ struct TileCfg {
   static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "even load split");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
   static_assert(STAGES >= 2, "at least double buffering");
-  static_assert(STAGES == 2 || (BK / KG) % 2 == 0, "ring pipeline alternates two operand sets");
+  static_assert(STAGES == 2 || (BK / KG / KS) % 2 == 0,
+                "ring pipeline alternates two operand sets per wave's share of a tile");
+  static_assert(KS == 1 || (KS == 2 && STAGES > 2), "K split in two, ring pipeline only");
+  // K split: group 1's accumulators pass through LDS to group 0 at the end.
+  static_assert(KS == 1 || (WGM * WGN) * RB * CB * TR::NACC * 64 <= STAGES * (A_STAGE + B_STAGE),
+                "K-split hand-over fits in the LDS ring");
 };
 
 // ---------------------------------------------------------------- loads
@@ -202,10 +207,10 @@ __device__ __forceinline__ typename TR::chunk_t load_chunk(const typename TR::T*
 }
 
 // ---------------------------------------------------------------- kernel
-template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES>
-__global__ void __launch_bounds__(WGM * WGN * 64)
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS>
+__global__ void __launch_bounds__(WGM * WGN * 64 * KS)
 gemm_tile_kernel(GemmArgs<typename TR::T> g) {
-  using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES>;
+  using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>;
   using T = typename TR::T;
   using chunk_t = typename TR::chunk_t;
   using acc_t = typename TR::acc_t;
@@ -220,7 +225,11 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wrow = (wave % WGM) * Cfg::WM, wcol = (wave / WGM) * Cfg::WN;
+  // KS groups of WGM x WGN waves; every group covers the whole tile and takes
+  // 1/KS of the inner-index groups of each K tile.
+  const int kgrp = (KS == 1) ? 0 : wave / (WGM * WGN);
+  const int wave_in = (KS == 1) ? wave : wave % (WGM * WGN);
+  const int wrow = (wave_in % WGM) * Cfg::WM, wcol = (wave_in / WGM) * Cfg::WN;
   const int M = g.M, N = g.N, K = g.K;
   const int lda = g.lda, ldb = g.ldb;
   const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
@@ -345,7 +354,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         for (int c = 0; c < CB; ++c) acc[b][c] = TR::mfma(o.a[s][b], o.b[c][s], acc[b][c]);
   };
 
-  constexpr int NG = BK / KG;
+  constexpr int NG = BK / KG;      // inner-index groups per K tile
+  constexpr int NGL = NG / KS;     // groups per K tile for one wave
+  const int kg0 = kgrp * NGL * KG; // this wave's first inner index in a tile
   const int nk = (K + BK - 1) / BK;
 
   if constexpr (STAGES == 2) {
@@ -406,7 +417,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     if (S - 1 < nk) gload(S - 1);
     __syncthreads();
     GroupOps ops[2];
-    read_ops(0, 0, ops[0]);
+    read_ops(0, kg0, ops[0]);
     // Drain those reads so that both edges into the loop header carry no
     // LDS operations in flight: otherwise the compiler's wait-count
     // insertion has to assume the prologue's reads are pending at every
@@ -418,7 +429,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     constexpr int N_WR = A_LOADS + B_LOADS;                        // ds_write
     constexpr int N_LD = A_LOADS + B_LOADS;                        // global loads
     constexpr int MPG = V * RB * CB;                                // MFMAs per group
-    constexpr bool INTERLEAVE = NG >= 2 && MPG >= N_WR + N_LD;
+    constexpr bool INTERLEAVE = NGL >= 2 && MPG >= N_WR + N_LD;
     int st = 0;                       // stage of tile kt
     int kt = 0;
     // Steady state, while tile kt+S exists and is whole (and the tile is
@@ -430,7 +441,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     for (; kt < nk_fast; ++kt) {
       const int st_next = (st + 1 == S) ? 0 : st + 1;
       const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
-      read_ops(st, KG, ops[1]);
+      read_ops(st, kg0 + KG, ops[1]);
       __builtin_amdgcn_sched_barrier(0);
       lstore(st_store);
       gload_full(kt + S);
@@ -450,10 +461,10 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int gi = 1; gi < NG; ++gi) {
+      for (int gi = 1; gi < NGL; ++gi) {
         // the next tile (kt+1 < nk_fast + S <= nk) always exists here
-        if (gi + 1 < NG) read_ops(st, (gi + 1) * KG, ops[(gi + 1) & 1]);
-        else read_ops(st_next, 0, ops[(gi + 1) & 1]);
+        if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
+        else read_ops(st_next, kg0, ops[(gi + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
         mma(ops[gi & 1]);
         __builtin_amdgcn_sched_barrier(0);
@@ -472,9 +483,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       if (kt + S - 1 < nk) lstore(st_store);
       if (kt + S < nk) gload(kt + S);
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        if (gi + 1 < NG) read_ops(st, (gi + 1) * KG, ops[(gi + 1) & 1]);
-        else read_ops(st_pf, 0, ops[(gi + 1) & 1]);
+      for (int gi = 0; gi < NGL; ++gi) {
+        if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
+        else read_ops(st_pf, kg0, ops[(gi + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
         mma(ops[gi & 1]);
         __builtin_amdgcn_sched_barrier(0);
@@ -482,6 +493,31 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       __syncthreads();
       st = st_next;
     }
+  }
+
+  if constexpr (KS == 2) {
+    // Group 1 hands its partial sums to group 0 through LDS (lane-linear,
+    // so each register index is one contiguous 256-byte row per wave); group
+    // 0 adds them in a fixed order and runs the epilogue alone.
+    constexpr int NREG = RB * CB * TR::NACC;
+    __syncthreads();                       // every wave is done with the ring
+    T* red = lds + wave_in * NREG * 64 + lane;
+    if (kgrp == 1) {
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int e = 0; e < TR::NACC; ++e) red[((b * CB + c) * TR::NACC + e) * 64] = acc[b][c][e];
+    }
+    __syncthreads();
+    if (kgrp == 1) return;
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int e = 0; e < TR::NACC; ++e) acc[b][c][e] += red[((b * CB + c) * TR::NACC + e) * 64];
   }
 
   // Epilogue.  A lane's accumulator registers come in runs of RUN_R

@@ -1,6 +1,6 @@
 // fp32 tile configurations (v_mfma_f32_32x32x2f32).
 //
-// Name: f32_<BM>x<BN>x<BK>_w<waves down>x<waves across>_s<LDS stages>_<vec|ua>.
+// Name: f32_<BM>x<BN>x<BK>_w<waves down>x<waves across>_s<LDS stages>[_k2]_<vec|ua>.
 // "vec" needs 16-byte aligned pointers and leading dimensions that are
 // multiples of 4; "ua" (unaligned) takes any element-aligned input and still
 // moves 16 bytes per global access.
@@ -11,6 +11,10 @@ namespace pgemm {
 #define PGEMM_F32(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                 \
   {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, \
    &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S>}
+// _k2: two groups of WM x WN waves split each K tile's inner indices.
+#define PGEMM_F32_K2(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                   \
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, \
+   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2>}
 
 // A host function owns the table so that it is never treated as device data.
 const Variant<float>* f32_variants(int* count) {
@@ -18,7 +22,10 @@ const Variant<float>* f32_variants(int* count) {
       // LDS ring of 3, 8 waves (2 per SIMD), wave tile 128 x 64: large problems
       PGEMM_F32(256, 256, 16, 2, 4, 3, true, vec),
       PGEMM_F32(256, 256, 16, 2, 4, 3, false, ua),
-      // LDS ring of 3, 8 waves, wave tile 32 x 64: fills 256 CUs from 2048^2
+      // 128 x 128 tiles fill 256 CUs from 2048^2: K split over two groups
+      // of 4 waves with 64 x 64 wave tiles (default), or 8 waves of 32 x 64
+      PGEMM_F32_K2(128, 128, 32, 2, 2, 3, true, vec),
+      PGEMM_F32_K2(128, 128, 32, 2, 2, 3, false, ua),
       PGEMM_F32(128, 128, 32, 4, 2, 3, true, vec),
       PGEMM_F32(128, 128, 32, 4, 2, 3, false, ua),
       PGEMM_F32(128, 128, 16, 4, 2, 4, true, vec),     // ring of 4, BK 16

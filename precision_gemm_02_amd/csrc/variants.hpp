@@ -19,7 +19,7 @@ struct Variant {
 };
 
 // Launch one tile configuration: one workgroup per BM x BN tile of C.
-template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES>
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS = 1>
 hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
   using T = typename TR::T;
   GemmArgs<T> g = a;
@@ -27,9 +27,9 @@ hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
   g.tiles_n = (g.N + BN - 1) / BN;
   if (g.group_m <= 0) g.group_m = 4;
   void* args[] = {&g};
-  const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(WGM * WGN * 64);
+  const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(WGM * WGN * 64 * KS);
   return hipLaunchKernel(reinterpret_cast<const void*>(
-                             &gemm_tile_kernel<TR, BM, BN, BK, WGM, WGN, VEC, STAGES>),
+                             &gemm_tile_kernel<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>),
                          grid, block, args, 0, stream);
 }
 

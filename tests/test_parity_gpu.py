@@ -184,7 +184,7 @@ def test_every_variant_exact_integer(variant):
 def ring_variants():
     out = []
     for v, n in pg.variants().items():
-        m = re.match(r"f(32|64)_(\d+)x(\d+)x(\d+)_w\d+x\d+_s(\d+)_(vec|ua)$", n)
+        m = re.match(r"f(32|64)_(\d+)x(\d+)x(\d+)_w\d+x\d+_s(\d+)(?:_k2)?_(vec|ua)$", n)
         if m and int(m.group(5)) > 2:
             out.append(v)
     return out
@@ -195,7 +195,7 @@ def test_ring_pipeline_boundaries(variant):
     """K around the start and end of the branch-free steady-state loop
     (which runs while tile kt+S is whole), and tiles partly outside C."""
     name = pg.variants()[variant]
-    m = re.match(r"f(32|64)_(\d+)x(\d+)x(\d+)_w\d+x\d+_s(\d+)_(vec|ua)$", name)
+    m = re.match(r"f(32|64)_(\d+)x(\d+)x(\d+)_w\d+x\d+_s(\d+)(?:_k2)?_(vec|ua)$", name)
     prec, BM, BN, BK, S, kind = m.group(1), int(m.group(2)), int(m.group(3)), \
         int(m.group(4)), int(m.group(5)), m.group(6)
     dtype = np.float32 if prec == "32" else np.float64
