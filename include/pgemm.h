@@ -35,6 +35,8 @@
 #ifndef PGEMM_H
 #define PGEMM_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -85,6 +87,33 @@ int gemm_f64(int m, int n, int k, double alpha, const double *A, int lda,
  */
 int matmat_f64(int lda, int ldb, int ldc, const double *A, const double *B,
                double *C, int N1, int N2, int N3, void *stream);
+
+/*
+ * Same as gemm_f32 / gemm_f64, with a caller-provided device workspace that
+ * lets the library balance the last, partly filled round of tiles: when the
+ * tiles of C do not divide evenly over the GPU's compute units, each
+ * leftover tile is split into slices of its inner dimension computed by
+ * otherwise idle compute units; their partial sums go to the workspace and a
+ * second kernel adds them, always in the same slice order, and applies
+ * alpha and beta.  Results stay deterministic (identical inputs give
+ * identical bits) but are not bitwise equal to gemm_f32's, whose summation
+ * order differs.
+ *
+ *   workspace        device pointer, 16-byte aligned (argument 12), or NULL
+ *   workspace_bytes  its size; pgemm_workspace_f32/f64(m, n, k) returns the
+ *                    size this shape can use (0 when no split applies)
+ * With NULL or a smaller workspace the call behaves exactly like gemm_f32.
+ * The workspace is scratch owned by the caller; calls that share one
+ * workspace must be ordered (e.g. on one stream).
+ */
+int gemm_f32_ws(int m, int n, int k, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc,
+                void *workspace, size_t workspace_bytes, void *stream);
+int gemm_f64_ws(int m, int n, int k, double alpha, const double *A, int lda,
+                const double *B, int ldb, double beta, double *C, int ldc,
+                void *workspace, size_t workspace_bytes, void *stream);
+size_t pgemm_workspace_f32(int m, int n, int k);
+size_t pgemm_workspace_f64(int m, int n, int k);
 
 /* Static text for a status code returned by any entry point. */
 const char *pgemm_status_string(int status);

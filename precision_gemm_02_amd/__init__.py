@@ -63,12 +63,20 @@ _lib.gemm_f32_variant.argtypes = [_i] + _lib.gemm_f32.argtypes
 _lib.gemm_f64_variant.argtypes = [_i] + _lib.gemm_f64.argtypes
 _lib.pgemm_select_f32.argtypes = [_i, _i, _i, _f, _vp, _i, _vp, _i, _f, _vp, _i]
 _lib.pgemm_select_f64.argtypes = [_i, _i, _i, _d, _vp, _i, _vp, _i, _d, _vp, _i]
+_sz = ctypes.c_size_t
+_lib.gemm_f32_ws.argtypes = _lib.gemm_f32.argtypes[:11] + [_vp, _sz, _vp]
+_lib.gemm_f64_ws.argtypes = _lib.gemm_f64.argtypes[:11] + [_vp, _sz, _vp]
+_lib.pgemm_workspace_f32.argtypes = [_i, _i, _i]
+_lib.pgemm_workspace_f64.argtypes = [_i, _i, _i]
+_lib.pgemm_workspace_f32.restype = _sz
+_lib.pgemm_workspace_f64.restype = _sz
 _lib.pgemm_status_string.argtypes = [_i]
 _lib.pgemm_status_string.restype = ctypes.c_char_p
 _lib.pgemm_variant_name.argtypes = [_i]
 _lib.pgemm_variant_name.restype = ctypes.c_char_p
 for _name in ("gemm_f32", "gemm_f64", "matmat_f64", "gemm_f32_variant", "gemm_f64_variant",
-              "pgemm_select_f32", "pgemm_select_f64", "pgemm_num_variants"):
+              "pgemm_select_f32", "pgemm_select_f64", "pgemm_num_variants", "gemm_f32_ws",
+              "gemm_f64_ws"):
     getattr(_lib, _name).restype = _i
 
 PGEMM_OK = 0
@@ -77,7 +85,8 @@ PGEMM_EVARIANT = -101
 
 EXPORTS = ("gemm_f32", "gemm_f64", "matmat_f64", "pgemm_status_string",
            "pgemm_select_f32", "pgemm_select_f64", "pgemm_variant_name",
-           "pgemm_num_variants", "gemm_f32_variant", "gemm_f64_variant")
+           "pgemm_num_variants", "gemm_f32_variant", "gemm_f64_variant",
+           "gemm_f32_ws", "gemm_f64_ws", "pgemm_workspace_f32", "pgemm_workspace_f64")
 
 
 class PgemmError(RuntimeError):
@@ -134,6 +143,27 @@ def matmat_f64(lda, ldb, ldc, A, B, C, N1, N2, N3, stream=None):
     """Row-major C(N1 x N3) += A(N1 x N2) * B(N2 x N3), fp64 (lecture form)."""
     _check(_lib.matmat_f64(lda, ldb, ldc, _addr(A), _addr(B), _addr(C), N1, N2, N3,
                            _stream(stream)), "matmat_f64")
+
+
+def gemm_f32_ws(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws, ws_bytes, stream=None):
+    """gemm_f32 with a device workspace for balancing leftover tiles."""
+    _check(_lib.gemm_f32_ws(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                            _addr(ws), ws_bytes, _stream(stream)), "gemm_f32_ws")
+
+
+def gemm_f64_ws(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws, ws_bytes, stream=None):
+    """gemm_f64 with a device workspace for balancing leftover tiles."""
+    _check(_lib.gemm_f64_ws(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
+                            _addr(ws), ws_bytes, _stream(stream)), "gemm_f64_ws")
+
+
+def workspace_f32(m, n, k) -> int:
+    """Workspace bytes gemm_f32_ws can use for this shape (0: none)."""
+    return _lib.pgemm_workspace_f32(m, n, k)
+
+
+def workspace_f64(m, n, k) -> int:
+    return _lib.pgemm_workspace_f64(m, n, k)
 
 
 def gemm_f32_variant(variant, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):

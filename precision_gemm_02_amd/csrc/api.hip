@@ -109,6 +109,48 @@ int choose_f64(int m, int n, bool vec) {
   return vec ? t.f64_small_vec : t.f64_small_ua;
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// Split of the last round of tiles.  With T tiles on P compute units, the
+// first R = floor(T/P) rounds stay one tile per workgroup; if the remaining
+// Tr = T - R*P tiles would leave most compute units idle in a last round,
+// each of them is split into s K slices (s*Tr <= P, at least 4 K tiles per
+// slice) whose partial sums go to the workspace and are added, in slice
+// order, by the fix-up kernel.
+struct SplitPlan {
+  int full_tiles = 0, split = 1;
+  size_t bytes = 0;
+};
+
+template <typename T>
+SplitPlan split_plan(const Variant<T>& v, int m, int n, int k, int cus) {
+  SplitPlan p;
+  const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
+  const long long rounds = tiles / cus, rest = tiles - rounds * cus;
+  const long long nk = ceil_div(k, v.bk);
+  if (rounds < 1 || rest == 0 || rest * 2 > cus) return p;
+  long long s = cus / rest;
+  if (s > nk / 4) s = nk / 4;
+  if (s < 2) return p;
+  p.full_tiles = (int)(rounds * cus);
+  p.split = (int)s;
+  p.bytes = (size_t)rest * (size_t)s * (size_t)v.bm * (size_t)v.bn * sizeof(T);
+  return p;
+}
+
 template <typename T>
 hipError_t launch_scale(int m, int n, T beta, T* C, int ldc, hipStream_t s) {
   if (beta == T(1)) return hipSuccess;
@@ -120,9 +162,17 @@ hipError_t launch_scale(int m, int n, T beta, T* C, int ldc, hipStream_t s) {
 
 template <typename T>
 int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, const T* B,
-        int ldb, T beta, T* C, int ldc, hipStream_t s) {
+        int ldb, T beta, T* C, int ldc, T* ws, size_t ws_bytes, hipStream_t s) {
   if (ceil_div(m, v.bm) * ceil_div(n, v.bn) > kMaxTiles) return PGEMM_EHIP;
   GemmArgs<T> g{};
+  if (ws != nullptr) {
+    const SplitPlan p = split_plan(v, m, n, k, device_cus());
+    if (p.split > 1 && ws_bytes >= p.bytes) {
+      g.full_tiles = p.full_tiles;
+      g.split = p.split;
+      g.ws = ws;
+    }
+  }
   g.M = m;
   g.N = n;
   g.K = k;
@@ -142,9 +192,10 @@ int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, 
 // forced < 0: choose; otherwise index into this precision's table.
 template <typename T>
 int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, const T* B,
-              int ldb, T beta, T* C, int ldc, void* stream) {
+              int ldb, T beta, T* C, int ldc, void* ws, size_t ws_bytes, void* stream) {
   const int st = check_args(m, n, k, alpha, A, lda, B, ldb, C, ldc);
   if (st != 0) return st;
+  if (ws != nullptr && !aligned16(ws)) return -12;
   if (m == 0 || n == 0) return PGEMM_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (k == 0 || alpha == T(0))
@@ -166,7 +217,19 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
     idx = forced;
     if (table[idx].vec && !vec) return PGEMM_EVARIANT;
   }
-  return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
+  return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+             static_cast<T*>(ws), ws_bytes, s);
+}
+
+// Workspace the split path would use for this shape (0: no split).
+template <typename T>
+size_t workspace_impl(int m, int n, int k) {
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  const Tables& t = tables();
+  // the aligned and unaligned variants of a shape class share their tiling
+  if constexpr (sizeof(T) == 4) return split_plan(t.f32[choose_f32(m, n, true)], m, n, k,
+                                                  device_cus()).bytes;
+  else return split_plan(t.f64[choose_f64(m, n, true)], m, n, k, device_cus()).bytes;
 }
 
 template <typename T>
@@ -189,13 +252,33 @@ extern "C" {
 
 int gemm_f32(int m, int n, int k, float alpha, const float* A, int lda, const float* B,
              int ldb, float beta, float* C, int ldc, void* stream) {
-  return gemm_impl<float>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+  return gemm_impl<float>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, 0,
+                          stream);
 }
 
 int gemm_f64(int m, int n, int k, double alpha, const double* A, int lda, const double* B,
              int ldb, double beta, double* C, int ldc, void* stream) {
-  return gemm_impl<double>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+  return gemm_impl<double>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, 0,
+                           stream);
 }
+
+int gemm_f32_ws(int m, int n, int k, float alpha, const float* A, int lda, const float* B,
+                int ldb, float beta, float* C, int ldc, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return gemm_impl<float>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                          workspace_bytes, stream);
+}
+
+int gemm_f64_ws(int m, int n, int k, double alpha, const double* A, int lda,
+                const double* B, int ldb, double beta, double* C, int ldc, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return gemm_impl<double>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                           workspace_bytes, stream);
+}
+
+size_t pgemm_workspace_f32(int m, int n, int k) { return workspace_impl<float>(m, n, k); }
+
+size_t pgemm_workspace_f64(int m, int n, int k) { return workspace_impl<double>(m, n, k); }
 
 // Row-major X (r x c, ld) is the column-major storage of X^T (c x r, ld), so
 // C^T = B^T A^T is a column-major GEMM with m = N3, n = N1, k = N2.
@@ -222,7 +305,7 @@ const char* pgemm_status_string(int status) {
     case PGEMM_EVARIANT: return "unknown or inapplicable kernel variant";
     default: break;
   }
-  if (status < 0 && status >= -12) return "invalid argument (see the argument position)";
+  if (status < 0 && status >= -14) return "invalid argument (see the argument position)";
   return "unknown status";
 }
 
@@ -250,7 +333,8 @@ const char* pgemm_variant_name(int variant) {
 int gemm_f32_variant(int variant, int m, int n, int k, float alpha, const float* A, int lda,
                      const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
   if (variant < 1 || variant > tables().n32) return PGEMM_EVARIANT;
-  return gemm_impl<float>(variant - 1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+  return gemm_impl<float>(variant - 1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, nullptr,
+                          0, stream);
 }
 
 int gemm_f64_variant(int variant, int m, int n, int k, double alpha, const double* A,
@@ -258,7 +342,8 @@ int gemm_f64_variant(int variant, int m, int n, int k, double alpha, const doubl
                      void* stream) {
   const int j = variant - 1 - tables().n32;
   if (j < 0 || j >= tables().n64) return PGEMM_EVARIANT;
-  return gemm_impl<double>(j, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+  return gemm_impl<double>(j, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, 0,
+                           stream);
 }
 
 }  // extern "C"

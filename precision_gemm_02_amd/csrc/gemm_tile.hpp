@@ -95,19 +95,29 @@ struct GemmArgs {
   int lda, ldb, ldc;
   int tiles_m, tiles_n;
   int group_m;     // tile rows per raster group
+  // Split of the last, partly filled round of tiles (see split_plan): the
+  // first `full_tiles` tiles (in raster order) get one workgroup each; each
+  // remaining tile gets `split` workgroups that take consecutive slices of
+  // its K tiles and write raw partial sums to `ws` (split == 0: no split).
+  int full_tiles;
+  int split;
+  T* ws;
 };
 
-// Workgroup id -> (tile row, tile column).
-// The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn, and
-// each XCD has its own L2.  Give every XCD one contiguous range of tile ids,
-// then walk tiles in groups of `group_m` tile rows so that the workgroups
-// resident on one XCD at the same time share A and B panels in its L2.
-__host__ __device__ inline void map_tile(int wg, int tiles_m, int tiles_n, int group_m,
-                                         int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
+// Workgroup id -> linear tile id, for `count` workgroups.  The dispatcher
+// hands consecutive workgroup ids to the 8 XCDs in turn, and each XCD has its
+// own L2: give every XCD one contiguous range of tile ids.
+__host__ __device__ inline int xcd_remap(int wg, int count) {
   const int xcd = wg & 7, local = wg >> 3;
-  const int base = total >> 3, rem = total & 7;
-  const int t = xcd * base + (xcd < rem ? xcd : rem) + local;
+  const int base = count >> 3, rem = count & 7;
+  return xcd * base + (xcd < rem ? xcd : rem) + local;
+}
+
+// Linear tile id -> (tile row, tile column), walking tiles in groups of
+// `group_m` tile rows so that the workgroups resident on one XCD at the same
+// time share A and B panels in its L2.
+__host__ __device__ inline void raster(int t, int tiles_m, int tiles_n, int group_m, int& tm,
+                                       int& tn) {
   const int per_group = group_m * tiles_n;
   const int group = t / per_group;
   const int first_m = group * group_m;
@@ -115,6 +125,11 @@ __host__ __device__ inline void map_tile(int wg, int tiles_m, int tiles_n, int g
   const int within = t - group * per_group;
   tm = first_m + within % gsize;
   tn = within / gsize;
+}
+
+__host__ __device__ inline void map_tile(int wg, int tiles_m, int tiles_n, int group_m,
+                                         int& tm, int& tn) {
+  raster(xcd_remap(wg, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 // XOR swizzle of the 16-byte chunks of one Bs row (KC chunks per row).  For
@@ -221,8 +236,21 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
 
   __shared__ __attribute__((aligned(16))) T lds[STAGES * (Cfg::A_STAGE + Cfg::B_STAGE)];
 
+  // Tile and range of K tiles of this workgroup.
+  const int nk_all = (g.K + BK - 1) / BK;
+  int t_lin, kt_begin = 0, kt_end = nk_all, slice = -1, r = 0;
+  if ((int)blockIdx.x < g.full_tiles) {
+    t_lin = xcd_remap(blockIdx.x, g.full_tiles);
+  } else {
+    const int u = blockIdx.x - g.full_tiles;
+    r = u / g.split;
+    slice = u - r * g.split;
+    t_lin = g.full_tiles + r;
+    kt_begin = (int)((long long)slice * nk_all / g.split);
+    kt_end = (int)((long long)(slice + 1) * nk_all / g.split);
+  }
   int tm, tn;
-  map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  raster(t_lin, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // KS groups of WGM x WGN waves; every group covers the whole tile and takes
@@ -357,7 +385,8 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   constexpr int NG = BK / KG;      // inner-index groups per K tile
   constexpr int NGL = NG / KS;     // groups per K tile for one wave
   const int kg0 = kgrp * NGL * KG; // this wave's first inner index in a tile
-  const int nk = (K + BK - 1) / BK;
+  // This workgroup's K tiles: [kt_begin, kt_end) (all of them unless the
+  // tile's K range is split over several workgroups).
 
   if constexpr (STAGES == 2) {
     // Two LDS stages.  Tile t+1 is fetched from HBM into registers while
@@ -389,14 +418,14 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         }
       }
     };
-    gload(0);
+    gload(kt_begin);
     lstore(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const bool more = kt + 1 < kt_end;
       if (more) gload(kt + 1);
-      compute(kt & 1);
-      if (more) lstore((kt + 1) & 1);
+      compute((kt - kt_begin) & 1);
+      if (more) lstore((kt + 1 - kt_begin) & 1);
       __syncthreads();
     }
   } else {
@@ -410,11 +439,11 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // start right after the barrier without waiting for LDS.
     constexpr int S = STAGES;
     for (int t = 0; t < S - 1; ++t)
-      if (t < nk) {
-        gload(t);
+      if (kt_begin + t < kt_end) {
+        gload(kt_begin + t);
         lstore(t);
       }
-    if (S - 1 < nk) gload(S - 1);
+    if (kt_begin + S - 1 < kt_end) gload(kt_begin + S - 1);
     __syncthreads();
     GroupOps ops[2];
     read_ops(0, kg0, ops[0]);
@@ -431,14 +460,15 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     constexpr int MPG = V * RB * CB;                                // MFMAs per group
     constexpr bool INTERLEAVE = NGL >= 2 && MPG >= N_WR + N_LD;
     int st = 0;                       // stage of tile kt
-    int kt = 0;
+    int kt = kt_begin;
     // Steady state, while tile kt+S exists and is whole (and the tile is
     // inside C): one branch-free block per iteration.  With in-order issue,
     // the tile's LDS stores and global loads are slotted one by one between
     // group 0's MFMAs (each executes while an MFMA occupies the matrix core)
     // instead of running as a block while the matrix core idles.
-    const int nk_fast = (INTERLEAVE && full_mn) ? max(0, K / BK - S) : 0;
-    for (; kt < nk_fast; ++kt) {
+    const int kt_fast_end =
+        (INTERLEAVE && full_mn) ? max(kt_begin, min(kt_end, K / BK) - S) : kt_begin;
+    for (; kt < kt_fast_end; ++kt) {
       const int st_next = (st + 1 == S) ? 0 : st + 1;
       const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
       read_ops(st, kg0 + KG, ops[1]);
@@ -462,7 +492,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int gi = 1; gi < NGL; ++gi) {
-        // the next tile (kt+1 < nk_fast + S <= nk) always exists here
+        // the next tile (kt+1 < kt_fast_end + S <= kt_end) always exists here
         if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
         else read_ops(st_next, kg0, ops[(gi + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
@@ -473,15 +503,15 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       st = st_next;
     }
     // Remaining iterations (edge tiles, the K tail, the last S tiles).
-    for (; kt < nk; ++kt) {
+    for (; kt < kt_end; ++kt) {
       const int st_next = (st + 1 == S) ? 0 : st + 1;
       const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
       // At the last tile the prefetch re-reads this tile's own stage (in
       // bounds, unused): a branch here would make the compiler wait for the
       // prefetch before the current group's MFMAs.
-      const int st_pf = (kt + 1 < nk) ? st_next : st;
-      if (kt + S - 1 < nk) lstore(st_store);
-      if (kt + S < nk) gload(kt + S);
+      const int st_pf = (kt + 1 < kt_end) ? st_next : st;
+      if (kt + S - 1 < kt_end) lstore(st_store);
+      if (kt + S < kt_end) gload(kt + S);
 #pragma unroll
       for (int gi = 0; gi < NGL; ++gi) {
         if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
@@ -525,20 +555,27 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   // row i at wave-tile row sb*MB*W + W*i + b', so for fixed (c, sb, run) the
   // lane owns RUN = RUN_R*W consecutive rows of one column: element o of
   // that run is register run*RUN_R + o/W of block sb*W + o%W.
-  const T alpha = g.alpha, beta = g.beta;
-  const int ldc = g.ldc;
+  // Destination: C, or for a K slice of a split tile its raw partial sums
+  // (alpha = 1, beta = 0, all BM x BN elements, column-major with ld = BM)
+  // in workspace slot (remainder tile r, slice).
+  const bool to_ws = slice >= 0;
+  T* const cbase = to_ws ? g.ws + (size_t)(r * g.split + slice) * (BM * BN) : g.C;
+  const int ldc = to_ws ? BM : g.ldc;
+  const T alpha = to_ws ? T(1) : g.alpha, beta = to_ws ? T(0) : g.beta;
+  const bool full_out = to_ws || full_mn;
+  const int row_off = to_ws ? 0 : m0, col_off = to_ws ? 0 : n0;
   constexpr int RUN = TR::RUN_R * W;
   constexpr int NRUN = TR::NACC / TR::RUN_R;
   constexpr bool VEC_C = (RUN % V == 0);   // whole 16-byte chunks per run
   const bool read_c = beta != T(0);
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
-    const int col = n0 + wcol + c * MB + lrow;
-    T* pcol = g.C + (size_t)col * ldc;
+    const int col = col_off + wcol + c * MB + lrow;
+    T* pcol = cbase + (size_t)col * ldc;
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
-      const int row0 = m0 + wrow + sb * MB * W;
-      if (full_mn) {
+      const int row0 = row_off + wrow + sb * MB * W;
+      if (full_out) {
         // Whole tile in range: issue every C load of this column block
         // first, then the multiply-adds and stores, so that the loads'
         // latency is paid once rather than once per run.
@@ -600,6 +637,28 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       }
     }
   }
+}
+
+// Fix-up of split tiles: C = alpha * (sum over the K slices, in slice order)
+// + beta * C for every element of the remainder tiles that lies inside C.
+// One thread per element; block y = remainder tile.
+template <typename T>
+__global__ void __launch_bounds__(256) split_fixup_kernel(GemmArgs<T> g, int bm, int bn) {
+  const int r = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;   // element of the tile, ld = bm
+  if (e >= bm * bn) return;
+  int tm, tn;
+  raster(g.full_tiles + r, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  const int i = tm * bm + e % bm, j = tn * bn + e / bm;
+  if (i >= g.M || j >= g.N) return;
+  const size_t slot = (size_t)bm * bn;
+  const T* p = g.ws + (size_t)r * g.split * slot + e;
+  T sum = p[0];
+  for (int sl = 1; sl < g.split; ++sl) sum += p[sl * slot];
+  T* pc = g.C + (size_t)j * g.ldc + i;
+  T v = g.alpha * sum;
+  if (g.beta != T(0)) v = __builtin_fma(g.beta, *pc, v);
+  *pc = v;
 }
 
 // C <- beta*C on the m x n block (the k == 0 / alpha == 0 path); beta == 0

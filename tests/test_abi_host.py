@@ -148,3 +148,28 @@ def test_binding_raises_on_bad_status():
     with pytest.raises(pg.PgemmError) as e:
         pg.gemm_f32(4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4, stream=0)
     assert e.value.status == -6
+
+
+def test_workspace_entry_points_host_checks():
+    ws32 = L.gemm_f32_ws
+    # ordinary argument errors keep their positions; a workspace that is not
+    # 16-byte aligned is argument 12
+    assert ws32(4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4, None, 0, None) == -6
+    assert ws32(4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4, FAKE + 4, 1 << 20, None) == -12
+    assert L.gemm_f64_ws(4, 4, 4, ctypes.c_double(1.0), FAKE, 4, FAKE, 4,
+                         ctypes.c_double(0.0), FAKE, 4, FAKE + 8, 1 << 20, None) == -12
+    # quick return with no memory touched
+    assert ws32(0, 4, 4, 1.0, None, 1, None, 4, 0.0, None, 1, None, 0, None) == 0
+
+
+def test_workspace_sizes():
+    # 8192^3: 1024 tiles of 256 x 256 fill whole rounds on 256 CUs -> no split
+    assert pg.workspace_f32(8192, 8192, 8192) == 0
+    assert pg.workspace_f32(2048, 2048, 2048) == 0
+    assert pg.workspace_f32(0, 10, 10) == 0 and pg.workspace_f32(10, 10, 0) == 0
+    # 4097 x 3001 x 1023 on 128 x 128 tiles: 33 x 24 = 792 tiles = 3 rounds of
+    # 256 + 24 leftover tiles, each split into 8 slices of 4 K tiles (32 in
+    # all).  256 compute units: the MI355X, and the fallback with no GPU.
+    assert pg.workspace_f32(4097, 3001, 1023) == 24 * 8 * 128 * 128 * 4
+    # too few K tiles to split (fewer than 8)
+    assert pg.workspace_f32(4097, 3001, 100) == 0

@@ -347,3 +347,87 @@ def test_python_gemm_layouts():
     pg.gemm(Acol, Bcol, Ccol, alpha=0.5, beta=2.0)
     assert_f32_parity(Ccol.cpu().numpy(), R, 200)
     assert torch.all(Ccol_store[:, 333:] == 0)
+
+
+# ------------------------------- split of the last round of tiles (workspace)
+def ws_size(p):
+    fn = pg.workspace_f32 if p.dtype == np.float32 else pg.workspace_f64
+    return fn(p.m, p.n, p.k)
+
+
+def run_ws(p, ws_bytes=None):
+    """gemm_*_ws with a guard-banded workspace of ws_bytes (default: the size
+    the library asks for); C, A, B and the workspace's margins are checked."""
+    need = ws_size(p)
+    nbytes = need if ws_bytes is None else ws_bytes
+    item = np.dtype(p.dtype).itemsize
+    welems = max(1, nbytes // item)
+    dW = DevMat(np.zeros(welems, p.dtype))
+    dA, dB, dC = DevMat(p.A), DevMat(p.B), DevMat(p.C)
+    fn = pg.gemm_f32_ws if p.dtype == np.float32 else pg.gemm_f64_ws
+    fn(p.m, p.n, p.k, p.alpha, dA.ptr, p.lda, dB.ptr, p.ldb, p.beta, dC.ptr, p.ldc,
+       dW.ptr, nbytes)
+    torch.cuda.synchronize()
+    dC.assert_untouched_outside(p.m, p.n, p.ldc)
+    dA.assert_untouched_outside(p.m, p.k, p.lda)
+    dB.assert_untouched_outside(p.k, p.n, p.ldb)
+    dW.assert_untouched_outside(welems, 1, welems)
+    return logical(dC.storage(), p.m, p.n, p.ldc).copy()
+
+
+# (dtype, m, n, k): each leaves a partly filled last round of tiles on 256
+# compute units and so takes the split path; they cover both tile classes of
+# each precision, ragged M/N edges inside the split tiles and a K tail in
+# the last slice.
+SPLIT_SHAPES = [
+    (np.float32, 2053, 2048, 1000),    # 128^2 tiles: 272 = 256 + 16, 8 slices
+    (np.float32, 2100, 2000, 555),     # 4 slices, K tail of 11
+    (np.float32, 4352, 4096, 640),     # 256^2 tiles: 272 tiles, 10 slices
+    (np.float64, 4200, 2048, 300),     # 256 x 128 tiles
+    (np.float64, 2100, 2000, 333),     # 128^2 fp64 tiles, K tail
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_SHAPES)))
+def test_split_exact_integer(case):
+    dtype, m, n, k = SPLIT_SHAPES[case]
+    alpha, beta = ALPHA_BETA[case % len(ALPHA_BETA)]
+    chunk = 4 if dtype == np.float32 else 2
+    lds = leading_dims(m, k, case % 2 == 0, chunk, case)
+    p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=300 + case)
+    assert ws_size(p) > 0, "shape no longer takes the split path"
+    say("split", np.dtype(dtype).name, (m, n, k), (alpha, beta), "ld", lds, "ws", ws_size(p))
+    C = run_ws(p)
+    assert_bitwise(C, oracle_full(p))
+
+
+def test_split_ragged_workload_parity():
+    p = gi.workload("sgemm_ragged")
+    assert ws_size(p) > 0
+    C = run_ws(p)
+    maxabs, rel = assert_f32_parity(C, oracle_full(p), p.k)
+    say("ragged split max|dC| %.3g rel %.3g" % (maxabs, rel))
+    q = gi.workload("sgemm_ragged", dist_override="i2")
+    assert_bitwise(run_ws(q), oracle_full(q))
+
+
+def test_split_fp64_parity():
+    p = gi.make_colmajor_problem("split64", np.float64, 2100, 2000, 333, 2101, 333, 2103,
+                                 0.75, -1.25, seed=31, dist="n", c_dist="n")
+    assert ws_size(p) > 0
+    assert_f64_parity(run_ws(p), oracle_full(p))
+
+
+def test_split_deterministic_and_small_workspace_is_plain():
+    p = gi.make_colmajor_problem("splitdet", np.float32, 2053, 2048, 1000, 2053, 1000, 2053,
+                                 1.5, 0.5, seed=32, dist="u", c_dist="u")
+    need = ws_size(p)
+    C1, C2 = run_ws(p), run_ws(p)
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
+    assert_f32_parity(C1, oracle_full(p), p.k)
+    # a workspace one chunk short (or none) gives exactly gemm_f32's result
+    plain, _ = run_colmajor(p)
+    short = run_ws(p, ws_bytes=need - 16)
+    assert np.array_equal(short.view(np.uint32), plain.view(np.uint32))
+    none = run_ws(p, ws_bytes=0)
+    assert np.array_equal(none.view(np.uint32), plain.view(np.uint32))
