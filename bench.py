@@ -1,7 +1,10 @@
 """Benchmark: GEMM TFLOPS of pgemm on one MI355X, with roofline and CPU baseline.
 
 One step = one call C <- alpha*A*B + beta*C through the C ABI on inputs that
-are already resident in HBM.  W untimed warmup steps, then K timed steps
+are already resident in HBM: gemm_f32 / gemm_f64, or gemm_*_ws with the
+workspace the library asks for when the tiles of C leave a partly filled last
+round (the 4097x3001x1023 workload), or matmat_f64 for the row-major fp64
+workload.  W untimed warmup steps, then K timed steps
 bracketed by torch.cuda.synchronize(); each timed launch is also bracketed by
 HIP events on the stream it is launched on, which gives the kernel's own
 average duration for the roofline figure.
@@ -83,19 +86,37 @@ class Resident:
         self.variant = pg.variants().get(sel(*self.args), "none")
         self.flops = 2.0 * p.m * p.n * p.k
         self.stream = torch.cuda.current_stream()
+        # A partly filled last round of tiles is split over K slices when the
+        # library is given the workspace it asks for (gemm_*_ws); shapes
+        # that fill whole rounds ask for none and use the plain entry point.
+        self.ws_bytes = 0
+        self.ws = None
+        if not p.rowmajor:
+            wsfn = pg.workspace_f32 if self.dt == "f32" else pg.workspace_f64
+            self.ws_bytes = int(wsfn(*self.args[:3]))
+            if self.ws_bytes > 0:
+                self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        if p.rowmajor:
+            self.entry = "matmat_f64"
+        else:
+            self.entry = ("gemm_%s_ws" if self.ws_bytes else "gemm_%s") % self.dt
 
     def launch(self):
         if self.p.rowmajor:
             p = self.p
             self.pg.matmat_f64(p.lda, p.ldb, p.ldc, self.A.data_ptr(), self.B.data_ptr(),
                                self.C.data_ptr(), p.m, p.k, p.n, self.stream)
+        elif self.ws_bytes:
+            fn = self.pg.gemm_f32_ws if self.dt == "f32" else self.pg.gemm_f64_ws
+            fn(*self.args, self.ws.data_ptr(), self.ws_bytes, stream=self.stream)
         elif self.dt == "f32":
             self.pg.gemm_f32(*self.args, stream=self.stream)
         else:
             self.pg.gemm_f64(*self.args, stream=self.stream)
 
     def reset_c(self):
-        self.C.copy_(self.C0)
+        if self.p.beta != 0:
+            self.C.copy_(self.C0)
 
     def algorithmic_bytes(self):
         p = self.p
@@ -117,6 +138,9 @@ def time_workload(r: Resident, steps: int, warmup: int, min_warm_s: float):
         n_warm += 1
         if n_warm % 8 == 0:
             torch.cuda.synchronize()
+        if n_warm % 64 == 0:
+            r.reset_c()   # beta != 0: keep C finite (|beta| > 1 grows it each call)
+    r.reset_c()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -177,6 +201,7 @@ def roofline(r: Resident, kern_ms_mean: float):
             "traffic": recorded_traffic(r.variant, r.name),
             "algorithmic_bytes": r.algorithmic_bytes(),
             "kernel": r.variant, "kernel_ms_mean": round(kern_ms_mean, 4),
+            "entry": r.entry, "workspace_bytes": r.ws_bytes,
             "source_digest": kernel_source_digest()}
 
 

@@ -463,7 +463,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     int kt = kt_begin;
     // Steady state, while tile kt+S exists and is whole (and the tile is
     // inside C): one branch-free block per iteration.  With in-order issue,
-    // the tile's LDS stores and global loads are slotted one by one between
+    // the tile's LDS stores and global loads are spread evenly between
     // group 0's MFMAs (each executes while an MFMA occupies the matrix core)
     // instead of running as a block while the matrix core idles.
     const int kt_fast_end =
@@ -477,17 +477,19 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       gload_full(kt + S);
       mma(ops[0]);
       if constexpr (INTERLEAVE) {
+        // spread evenly: SP MFMAs before each store and each load
+        constexpr int SP = MPG / (N_WR + N_LD);
 #pragma unroll
         for (int i = 0; i < N_WR; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+          __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
         }
 #pragma unroll
         for (int i = 0; i < N_LD; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+          __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MPG - N_WR - N_LD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MPG - SP * (N_WR + N_LD), 0);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
