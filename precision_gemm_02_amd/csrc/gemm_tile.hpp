@@ -459,30 +459,58 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // no-wait maxima.)
     __builtin_amdgcn_s_waitcnt(0xC07F);
     // Instruction counts of one iteration, for the interleave below.
+    constexpr int N_RD = CB + V * SB;                              // ds_read per group
     constexpr int N_WR = A_LOADS + B_LOADS;                        // ds_write
     constexpr int N_LD = A_LOADS + B_LOADS;                        // global loads
     constexpr int MPG = V * RB * CB;                                // MFMAs per group
     constexpr bool INTERLEAVE = NGL >= 2 && MPG >= N_WR + N_LD;
+    // Operand reads too, one between MFMAs, when a group has room for them.
+    // After each barrier every wave starts the same group at once; reads
+    // issued as a block then queue behind the other waves' reads, and both
+    // waves of a SIMD stall with the matrix core idle.
+    constexpr bool READS_SPREAD = MPG >= N_RD;
+    constexpr bool RIL = INTERLEAVE && MPG >= N_RD + N_WR + N_LD;
+    // Schedule: the operand reads of the next group one per MFMA, then the
+    // rest of the group's MFMAs (groups without stores or loads).
+    auto spread_reads = [&]() {
+      if constexpr (READS_SPREAD) {
+#pragma unroll
+        for (int i = 0; i < N_RD; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MPG - N_RD, 0);
+      }
+    };
     int st = 0;                       // stage of tile kt
     int kt = kt_begin;
     // Steady state, while tile kt+S exists and is whole (and the tile is
     // inside C): one branch-free block per iteration.  With in-order issue,
-    // the tile's LDS stores and global loads are spread evenly between
-    // group 0's MFMAs (each executes while an MFMA occupies the matrix core)
-    // instead of running as a block while the matrix core idles.
+    // the next group's operand reads, the tile's LDS stores and its global
+    // loads are spread evenly between group 0's MFMAs (each executes while
+    // an MFMA occupies the matrix core) instead of running as a block while
+    // the matrix core idles.
     const int kt_fast_end =
         (INTERLEAVE && full_mn) ? max(kt_begin, min(kt_end, K / BK) - S) : kt_begin;
     for (; kt < kt_fast_end; ++kt) {
       const int st_next = (st + 1 == S) ? 0 : st + 1;
       const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
       read_ops(st, kg0 + KG, ops[1]);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!RIL) __builtin_amdgcn_sched_barrier(0);
       lstore(st_store);
       gload_full(kt + S);
       mma(ops[0]);
       if constexpr (INTERLEAVE) {
-        // spread evenly: SP MFMAs before each store and each load
-        constexpr int SP = MPG / (N_WR + N_LD);
+        // spread evenly: SP MFMAs before each read, store and load
+        constexpr int NM = (RIL ? N_RD : 0) + N_WR + N_LD;
+        constexpr int SP = MPG / NM;
+        if constexpr (RIL) {
+#pragma unroll
+          for (int i = 0; i < N_RD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+          }
+        }
 #pragma unroll
         for (int i = 0; i < N_WR; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
@@ -493,7 +521,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
           __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MPG - SP * (N_WR + N_LD), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MPG - SP * NM, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -501,8 +529,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         // the next tile (kt+1 < kt_fast_end + S <= kt_end) always exists here
         if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
         else read_ops(st_next, kg0, ops[(gi + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
         mma(ops[gi & 1]);
+        spread_reads();
         __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
@@ -522,8 +551,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       for (int gi = 0; gi < NGL; ++gi) {
         if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
         else read_ops(st_pf, kg0, ops[(gi + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
         mma(ops[gi & 1]);
+        spread_reads();
         __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
