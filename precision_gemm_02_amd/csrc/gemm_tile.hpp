@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pgemm {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -168,6 +170,14 @@ struct TileCfg {
   static constexpr int A_CHUNKS = A_STAGE / V, B_CHUNKS = B_STAGE / V;
   static constexpr int A_LOADS = A_CHUNKS / NT, B_LOADS = B_CHUNKS / NT;
   static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * (int)sizeof(T);
+  // 32-bit registers per lane: accumulators, two operand sets, staging.
+  static constexpr int ACC_REGS = RB * CB * TR::NACC * (int)sizeof(T) / 4;
+  static constexpr int OPS_REGS = (CB * V + V * RB) * (int)sizeof(T) / 4;
+  static constexpr int STAGE_REGS = (A_LOADS + B_LOADS) * 4;
+  // Unroll the steady-state loop by the ring depth (compile-time stages, no
+  // LDS address arithmetic) when that leaves room for the addresses it keeps
+  // live; larger tiles would spill.
+  static constexpr bool UNROLL = ACC_REGS + 2 * OPS_REGS + STAGE_REGS <= 192;
   static_assert(WM * WGM == BM && WN * WGN == BN, "waves tile the block");
   static_assert(RB * TR::MB == WM && CB * TR::MB == WN, "blocks tile the wave");
   static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8, "row blocks");
@@ -182,6 +192,16 @@ struct TileCfg {
   static_assert(KS == 1 || (WGM * WGN) * RB * CB * TR::NACC * 64 <= STAGES * (A_STAGE + B_STAGE),
                 "K-split hand-over fits in the LDS ring");
 };
+
+// f(integral_constant<int, I>) for I = FIRST .. LAST-1, unrolled at compile
+// time (so that an LDS stage index becomes an immediate offset).
+template <int I, int LAST, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < LAST) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, LAST>(f);
+  }
+}
 
 // ---------------------------------------------------------------- loads
 // 16 bytes at p.  VEC: p is 16-byte aligned.  Otherwise p is only element
@@ -238,6 +258,8 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   constexpr int KG = Cfg::KG, KC = Cfg::KC;
   constexpr int A_LOADS = Cfg::A_LOADS, B_LOADS = Cfg::B_LOADS;
 
+  // LDS: the A stages, then the B stages (so that, with a compile-time
+  // stage, an access is one per-thread base plus an immediate offset).
   __shared__ __attribute__((aligned(16))) T lds[STAGES * (Cfg::A_STAGE + Cfg::B_STAGE)];
 
   // Tile and range of K tiles of this workgroup.
@@ -271,21 +293,22 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   //  B: column q / KC, inner indices (q % KC)*V .. +V-1 of the tile.
   chunk_t ra[A_LOADS], rb[B_LOADS];
 
-  // Whole tile in range: unmasked loads, no branches.
+  // Whole tile in range: unmasked loads, no branches.  A thread's chunks
+  // i = 0, 1, ... of a tile lie NT/(BM/V) columns of A (NT/KC columns of B)
+  // apart, so one address per operand is formed up front; chunk i of tile
+  // kt adds a uniform offset, one 64-bit add per load.
+  static_assert(NT % (BM / V) == 0 && NT % KC == 0, "uniform steps between a thread's chunks");
+  const T* const pa0 = g.A + (size_t)(tid / (BM / V)) * lda + (m0 + (tid % (BM / V)) * V);
+  const T* const pb0 = g.B + (size_t)(n0 + tid / KC) * ldb + (tid % KC) * V;
   auto gload_full = [&](int kt) {
-    const int k0 = kt * BK;
+    const size_t astep = (size_t)kt * BK * (size_t)lda;
+    const int bstep = kt * BK;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int q = tid + i * NT;
-      const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
-      ra[i] = load_chunk_full<TR, VEC>(g.A + (size_t)(k0 + kk) * lda + (m0 + mm));
-    }
+    for (int i = 0; i < A_LOADS; ++i)
+      ra[i] = load_chunk_full<TR, VEC>(pa0 + (astep + (size_t)(i * (NT / (BM / V))) * lda));
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int q = tid + i * NT;
-      const int nn = q / KC, kk = (q % KC) * V;
-      rb[i] = load_chunk_full<TR, VEC>(g.B + (size_t)(n0 + nn) * ldb + (k0 + kk));
-    }
+    for (int i = 0; i < B_LOADS; ++i)
+      rb[i] = load_chunk_full<TR, VEC>(pb0 + ((size_t)(i * (NT / KC)) * ldb + bstep));
   };
   // Edge tiles and the K tail: out-of-range elements load as zero.
   auto gload_masked = [&](int kt) {
@@ -315,8 +338,8 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   };
 
   auto lstore = [&](int stage) {
-    T* As = lds + stage * (Cfg::A_STAGE + Cfg::B_STAGE);
-    T* Bs = As + Cfg::A_STAGE;
+    T* As = lds + stage * Cfg::A_STAGE;
+    T* Bs = lds + STAGES * Cfg::A_STAGE + stage * Cfg::B_STAGE;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int q = tid + i * NT;
@@ -348,8 +371,8 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     T a[V][RB];
   };
   auto read_ops = [&](int stage, int kg, GroupOps& o) {
-    const T* As = lds + stage * (Cfg::A_STAGE + Cfg::B_STAGE);
-    const T* Bs = As + Cfg::A_STAGE;
+    const T* As = lds + stage * Cfg::A_STAGE;
+    const T* Bs = lds + STAGES * Cfg::A_STAGE + stage * Cfg::B_STAGE;
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       const int n = wcol + c * MB + lrow;
@@ -492,7 +515,10 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // the matrix core idles.
     const int kt_fast_end =
         (INTERLEAVE && full_mn) ? max(kt_begin, min(kt_end, K / BK) - S) : kt_begin;
-    for (; kt < kt_fast_end; ++kt) {
+    // The steady state is unrolled by S, so that every stage index is a
+    // compile-time constant and each LDS access is a per-thread base plus an
+    // immediate offset (no address arithmetic per iteration).
+    auto fast_iteration = [&](const int st, const int kt) __attribute__((always_inline)) {
       const int st_next = (st + 1 == S) ? 0 : st + 1;
       const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
       read_ops(st, kg0 + KG, ops[1]);
@@ -535,7 +561,17 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
-      st = st_next;
+    };
+    // st == 0 here (kt == kt_begin), and after every S iterations
+    if constexpr (Cfg::UNROLL) {
+      for (; kt + S <= kt_fast_end; kt += S)
+        static_for<0, S>([&](auto st_c) {
+          fast_iteration(decltype(st_c)::value, kt + decltype(st_c)::value);
+        });
+    }
+    for (; kt < kt_fast_end; ++kt) {
+      fast_iteration(st, kt);
+      st = (st + 1 == S) ? 0 : st + 1;
     }
     // Remaining iterations (edge tiles, the K tail, the last S tiles).
     for (; kt < kt_end; ++kt) {
