@@ -15,12 +15,14 @@ namespace pgemm {
 // A host function owns the table so that it is never treated as device data.
 const Variant<double>* f64_variants(int* count) {
   static const Variant<double> table[] = {
-      // LDS ring of 3, 8 waves, wave tile 64 x 64: large problems
-      PGEMM_F64(256, 128, 16, 4, 2, 3, true, vec),
-      PGEMM_F64(256, 128, 16, 4, 2, 3, false, ua),
-      // LDS ring of 3, 8 waves, wave tile 64 x 32: smaller problems
+      // LDS ring of 3, 8 waves, wave tile 64 x 32, unrolled steady state:
+      // the default at every size
       PGEMM_F64(128, 128, 16, 2, 4, 3, true, vec),
       PGEMM_F64(128, 128, 16, 2, 4, 3, false, ua),
+      // LDS ring of 3, 8 waves, wave tile 64 x 64 (too many registers to
+      // unroll the steady state)
+      PGEMM_F64(256, 128, 16, 4, 2, 3, true, vec),
+      PGEMM_F64(256, 128, 16, 4, 2, 3, false, ua),
       // plain double buffering
       PGEMM_F64(256, 128, 16, 2, 4, 2, true, vec),
       PGEMM_F64(128, 128, 16, 2, 2, 2, true, vec),

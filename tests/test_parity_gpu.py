@@ -200,8 +200,11 @@ def test_ring_pipeline_boundaries(variant):
         int(m.group(4)), int(m.group(5)), m.group(6)
     dtype = np.float32 if prec == "32" else np.float64
     chunk = 4 if dtype == np.float32 else 2
+    # whole K tiles nk: the steady-state loop runs nk - S iterations, first in
+    # trips of S (compile-time stages), then 0..S-1 more with a runtime stage
     Ks = sorted({1, BK - 1, BK * (S - 1), BK * S, BK * S + 1, BK * (S + 1) - 1,
-                 BK * (S + 1), BK * (S + 1) + 1, BK * (S + 2) + 3, BK * (2 * S + 3)})
+                 BK * (S + 1), BK * (S + 1) + 1, BK * (S + 2) + 3, BK * (2 * S + 1),
+                 BK * (2 * S + 2), BK * (2 * S + 3), BK * (3 * S + 2) + 5})
     shapes = [(2 * BM, 2 * BN), (2 * BM + 5, BN + 3)]
     t = 0
     for (mm, nn) in shapes:
@@ -383,7 +386,7 @@ SPLIT_SHAPES = [
     (np.float32, 2053, 2048, 1000),    # 128^2 tiles: 272 = 256 + 16, 8 slices
     (np.float32, 2100, 2000, 555),     # 4 slices, K tail of 11
     (np.float32, 4352, 4096, 640),     # 256^2 tiles: 272 tiles, 10 slices
-    (np.float64, 4200, 2048, 300),     # 256 x 128 tiles
+    (np.float64, 4200, 2048, 300),     # 128^2 fp64 tiles: 528 = 2*256 + 16
     (np.float64, 2100, 2000, 333),     # 128^2 fp64 tiles, K tail
 ]
 
