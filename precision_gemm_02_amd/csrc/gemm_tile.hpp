@@ -14,9 +14,9 @@
 //    become one wave-level tile of RB x CB matrix-core blocks whose
 //    accumulators stay in registers for the whole K loop.
 //  * Double buffering / prefetch (SGEMM study kernel 10; V3 page measure
-//    (2)): two LDS stages; the next K tile is fetched from HBM into registers
-//    while the current one feeds the matrix cores, then written to the other
-//    stage; one workgroup barrier per K tile.
+//    (2)) becomes a ring of LDS stages: the next K tiles are fetched from HBM
+//    into registers while the current one feeds the matrix cores, then
+//    written to a free stage; one workgroup barrier per K tile.
 //  * Bank-conflict fixes (V3 page, sections V3.1 and V3.2): column-major A
 //    arrives m-contiguous and is stored as As[k][m] with no transpose, so its
 //    16-byte writes and reads are contiguous per lane group; B arrives
