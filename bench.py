@@ -157,28 +157,25 @@ def time_workload(r: Resident, steps: int, warmup: int, min_warm_s: float):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-CSRC = os.path.join(ROOT, "precision_gemm_02_amd", "csrc")
+LIB = os.path.join(ROOT, "precision_gemm_02_amd", "libpgemm.so")
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the kernel sources and build script (identifies a build)."""
+def library_digest() -> str:
+    """sha256 of the built libpgemm.so (the code that runs; the build is
+    deterministic, so a change to comments alone keeps the digest)."""
     import hashlib
-    h = hashlib.sha256()
-    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
-    for f in files:
-        h.update(f.encode())
-        h.update(open(os.path.join(CSRC, f), "rb").read())
-    h.update(open(os.path.join(ROOT, "precision_gemm_02_amd", "build.py"), "rb").read())
-    return h.hexdigest()[:16]
+    if not os.path.exists(LIB):
+        return "unbuilt"
+    return hashlib.sha256(open(LIB, "rb").read()).hexdigest()[:16]
 
 
 def recorded_traffic(variant: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 counter runs, as recorded in
     profiles/*counters*.md, or None if none matches this variant, workload
-    and the current kernel sources (the kernel changed since it was taken)."""
+    and the built library (the kernel changed since it was taken)."""
     if not os.path.isdir(PROFILES):
         return None
-    digest = kernel_source_digest()
+    digest = library_digest()
     for f in sorted(os.listdir(PROFILES)):
         if "counters" not in f:
             continue
@@ -188,7 +185,7 @@ def recorded_traffic(variant: str, workload: str):
                 k, v = line[2:].strip().split(": ", 1)
                 kv[k.strip("`")] = v.strip().strip("`")
         if (kv.get("variant") == variant and kv.get("workload") == workload
-                and kv.get("source_digest") == digest and "traffic_bytes_per_launch" in kv):
+                and kv.get("library_digest") == digest and "traffic_bytes_per_launch" in kv):
             return float(kv["traffic_bytes_per_launch"])
     return None
 
@@ -202,7 +199,7 @@ def roofline(r: Resident, kern_ms_mean: float):
             "algorithmic_bytes": r.algorithmic_bytes(),
             "kernel": r.variant, "kernel_ms_mean": round(kern_ms_mean, 4),
             "entry": r.entry, "workspace_bytes": r.ws_bytes,
-            "source_digest": kernel_source_digest()}
+            "library_digest": library_digest()}
 
 
 def cpu_baseline(p, first_out: np.ndarray, seconds: float):

@@ -37,9 +37,9 @@ def test_gpus_above_one_exits_with_message():
 
 def test_recorded_traffic_requires_matching_sources(tmp_path, monkeypatch):
     import bench
-    d = bench.kernel_source_digest()
+    d = bench.library_digest()
     f = tmp_path / "x_counters.md"
-    f.write_text("- `variant`: `v1`\n- `workload`: `w1`\n- `source_digest`: `%s`\n"
+    f.write_text("- `variant`: `v1`\n- `workload`: `w1`\n- `library_digest`: `%s`\n"
                  "- `traffic_bytes_per_launch`: `123`\n" % d)
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.recorded_traffic("v1", "w1") == 123.0
