@@ -434,3 +434,42 @@ def test_split_deterministic_and_small_workspace_is_plain():
     assert np.array_equal(short.view(np.uint32), plain.view(np.uint32))
     none = run_ws(p, ws_bytes=0)
     assert np.array_equal(none.view(np.uint32), plain.view(np.uint32))
+
+
+# ------------------------------------------------------ 64-bit addressing
+def _big_storage(logical_cm, rows, cols, ld, dtype):
+    """Device storage of a column-major (rows x cols) matrix with leading
+    dimension ld (possibly > 2^31 elements in all), zeros elsewhere."""
+    t = torch.zeros(ld * cols, dtype=dtype, device="cuda")
+    t.view(cols, ld)[:, :rows] = torch.from_numpy(np.ascontiguousarray(logical_cm.T)).cuda()
+    return t
+
+
+@pytest.mark.parametrize("which,dtype", [("A", np.float32), ("B", np.float32), ("C", np.float32),
+                                         ("C", np.float64)])
+def test_storage_beyond_2_31_elements(which, dtype):
+    """One operand's leading dimension puts its last columns more than 2^31
+    elements (and 2^32 bytes) past its base: every address in the load and
+    store paths must be formed in 64 bits."""
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    m, n, k = 300, 2100, 2100
+    big = 1 << 21                       # ld * 2100 columns > 2^32 elements
+    lda, ldb, ldc = (big if which == "A" else m), (big if which == "B" else k), \
+        (big if which == "C" else m)
+    p = exact_problem(dtype, m, n, k, 0.75, -1.25, (m, k, m), seed=400)
+    A = logical(p.A, m, k, m)
+    B = logical(p.B, k, n, k)
+    C0 = logical(p.C, m, n, m)
+    say("64-bit", which, np.dtype(dtype).name, "ld", (lda, ldb, ldc))
+    dA = _big_storage(A, m, k, lda, tdt)
+    dB = _big_storage(B, k, n, ldb, tdt)
+    dC = _big_storage(C0, m, n, ldc, tdt)
+    fn = pg.gemm_f32 if dtype == np.float32 else pg.gemm_f64
+    fn(m, n, k, p.alpha, dA, lda, dB, ldb, p.beta, dC, ldc)
+    torch.cuda.synchronize()
+    got = dC.view(n, ldc)[:, :m].t().cpu().numpy()
+    pad = dC.view(n, ldc)[:, m:m + 64]
+    assert bool((pad == 0).all()), "write into leading-dimension padding"
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    assert_bitwise(got, oracle_full(p))
