@@ -13,11 +13,15 @@
  *   padding rows between the logical extent and the leading dimension are
  *   never read (A, B) and never written (C).
  * Memory.  A, B, C are DEVICE pointers on the current HIP device, owned by
- *   the caller.  The library allocates nothing per call and keeps no state
- *   besides read-only kernel code.  C must not overlap A or B; A may equal B.
+ *   the caller (matmat_f64_host alone takes host pointers).  The library
+ *   allocates nothing per call and keeps no state besides read-only kernel
+ *   code and a per-device compute-unit count; scratch memory, where an entry
+ *   point uses any, is a caller workspace.  C must not overlap A or B; A may
+ *   equal B.
  * Stream.  `stream` is a hipStream_t passed as void*; NULL means the default
  *   stream.  Every call is stream-ordered and asynchronous: it returns after
- *   enqueueing work; the caller synchronizes.
+ *   enqueueing work; the caller synchronizes (matmat_f64_host alone returns
+ *   after its result is back in host memory).
  * Semantics (BLAS convention where the pages are silent).
  *   m == 0 or n == 0: nothing is touched, returns 0.
  *   k == 0 or alpha == 0: C <- beta*C; A and B are not read (may be NULL).
@@ -28,8 +32,8 @@
  *   given build is deterministic: identical inputs give identical bits.
  * Errors.  Returns 0 on success.  An invalid argument returns -p, where p is
  *   the 1-based position of the first offending argument in the signature
- *   (e.g. -6 for a bad lda in gemm_f32).  A failed kernel launch returns
- *   PGEMM_EHIP.  Nothing aborts and nothing prints.  Argument checking
+ *   (e.g. -6 for a bad lda in gemm_f32).  A failed kernel launch (or copy)
+ *   returns PGEMM_EHIP.  Nothing aborts and nothing prints.  Argument checking
  *   happens before any HIP call.
  */
 #ifndef PGEMM_H
@@ -42,7 +46,7 @@ extern "C" {
 #endif
 
 #define PGEMM_OK 0
-#define PGEMM_EHIP (-100)      /* a HIP launch reported an error */
+#define PGEMM_EHIP (-100)      /* a HIP launch, copy or synchronization failed */
 #define PGEMM_EVARIANT (-101)  /* unknown kernel variant id */
 
 /*
@@ -114,6 +118,33 @@ int gemm_f64_ws(int m, int n, int k, double alpha, const double *A, int lda,
                 void *workspace, size_t workspace_bytes, void *stream);
 size_t pgemm_workspace_f32(int m, int n, int k);
 size_t pgemm_workspace_f64(int m, int n, int k);
+
+/*
+ * The lecture's matmat on HOST memory ("HPC - Lecture 13 - MatMat GPU",
+ * section "function matmatgpu1": A, B, C start in host memory, go to the
+ * device, the kernel runs, C comes back).  Same arguments and meaning as
+ * matmat_f64 (row-major, C <- C + A*B), but A, B, C are host pointers, plus
+ * a caller-owned DEVICE workspace that receives copies of the three
+ * matrices with the same leading dimensions:
+ *   workspace        device pointer, 16-byte aligned            (argument 10)
+ *   workspace_bytes  at least pgemm_matmat_host_workspace(lda, ldb, ldc,
+ *                    N1, N2, N3)                                (argument 11)
+ * Each operand moves as one flat copy of its strided block (the padding
+ * between rows is read but never used; flat copies are much faster than
+ * pitched ones from pageable memory), the product runs as matmat_f64 on the
+ * workspace copies, and C's N1 x N3 block comes back (row by row when ldc >
+ * N3: the padding of C is never written).  The call returns after C is back
+ * in host memory (it synchronizes `stream`).  Pinned host memory transfers
+ * faster than pageable.  N1 = 0, N3 = 0 or N2 = 0 return 0 without touching
+ * memory (C + A*B = C when N2 = 0).  PGEMM_EHIP if a copy, the launch or the
+ * synchronization fails.
+ */
+int matmat_f64_host(int lda, int ldb, int ldc, const double *A, const double *B,
+                    double *C, int N1, int N2, int N3, void *workspace,
+                    size_t workspace_bytes, void *stream);
+/* Workspace bytes matmat_f64_host needs (0 for an empty product or invalid
+ * leading dimensions). */
+size_t pgemm_matmat_host_workspace(int lda, int ldb, int ldc, int N1, int N2, int N3);
 
 /* Static text for a status code returned by any entry point. */
 const char *pgemm_status_string(int status);

@@ -70,6 +70,10 @@ _lib.pgemm_workspace_f32.argtypes = [_i, _i, _i]
 _lib.pgemm_workspace_f64.argtypes = [_i, _i, _i]
 _lib.pgemm_workspace_f32.restype = _sz
 _lib.pgemm_workspace_f64.restype = _sz
+_lib.matmat_f64_host.argtypes = [_i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]
+_lib.matmat_f64_host.restype = _i
+_lib.pgemm_matmat_host_workspace.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.pgemm_matmat_host_workspace.restype = _sz
 _lib.pgemm_status_string.argtypes = [_i]
 _lib.pgemm_status_string.restype = ctypes.c_char_p
 _lib.pgemm_variant_name.argtypes = [_i]
@@ -86,7 +90,8 @@ PGEMM_EVARIANT = -101
 EXPORTS = ("gemm_f32", "gemm_f64", "matmat_f64", "pgemm_status_string",
            "pgemm_select_f32", "pgemm_select_f64", "pgemm_variant_name",
            "pgemm_num_variants", "gemm_f32_variant", "gemm_f64_variant",
-           "gemm_f32_ws", "gemm_f64_ws", "pgemm_workspace_f32", "pgemm_workspace_f64")
+           "gemm_f32_ws", "gemm_f64_ws", "pgemm_workspace_f32", "pgemm_workspace_f64",
+           "matmat_f64_host", "pgemm_matmat_host_workspace")
 
 
 class PgemmError(RuntimeError):
@@ -164,6 +169,29 @@ def workspace_f32(m, n, k) -> int:
 
 def workspace_f64(m, n, k) -> int:
     return _lib.pgemm_workspace_f64(m, n, k)
+
+
+def _host_addr(x):
+    """Host address of a numpy array (its data pointer) or an int; None -> NULL."""
+    if x is None or isinstance(x, int):
+        return x
+    if not x.flags["C_CONTIGUOUS"] and not x.flags["F_CONTIGUOUS"]:
+        raise ValueError("host arrays must be contiguous storage")
+    return x.ctypes.data
+
+
+def matmat_f64_host(lda, ldb, ldc, A, B, C, N1, N2, N3, ws, ws_bytes, stream=None):
+    """Lecture matmat (row-major, C += A*B) on host arrays (numpy float64
+    storage or int addresses) with a device workspace; returns when C is back
+    in host memory."""
+    _check(_lib.matmat_f64_host(lda, ldb, ldc, _host_addr(A), _host_addr(B), _host_addr(C),
+                                N1, N2, N3, _addr(ws), ws_bytes, _stream(stream)),
+           "matmat_f64_host")
+
+
+def matmat_host_workspace(lda, ldb, ldc, N1, N2, N3) -> int:
+    """Device workspace bytes matmat_f64_host needs."""
+    return _lib.pgemm_matmat_host_workspace(lda, ldb, ldc, N1, N2, N3)
 
 
 def gemm_f32_variant(variant, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):

@@ -173,3 +173,37 @@ def test_workspace_sizes():
     assert pg.workspace_f32(4097, 3001, 1023) == 24 * 8 * 128 * 128 * 4
     # too few K tiles to split (fewer than 8)
     assert pg.workspace_f32(4097, 3001, 100) == 0
+
+
+def test_matmat_host_argument_codes_and_quick_returns():
+    mm = L.matmat_f64_host
+    ws = FAKE
+    need = pg.matmat_host_workspace(8, 8, 8, 8, 8, 8)
+    ok = [8, 8, 8, FAKE, FAKE, FAKE, 8, 8, 8, ws, need, None]
+    for pos, bad in ((1, 7), (2, 7), (3, 7)):
+        args = list(ok)
+        args[pos - 1] = bad
+        assert mm(*args) == -pos
+    for pos in (4, 5, 6):
+        args = list(ok)
+        args[pos - 1] = None
+        assert mm(*args) == -pos
+    args = list(ok); args[9] = None; assert mm(*args) == -10
+    args = list(ok); args[9] = FAKE + 8; assert mm(*args) == -10    # not 16-byte aligned
+    args = list(ok); args[10] = need - 1; assert mm(*args) == -11
+    # empty C, or N2 = 0 (C + A*B = C): nothing touched, no workspace needed
+    assert mm(8, 8, 8, None, None, None, 0, 8, 8, None, 0, None) == 0
+    assert mm(1, 8, 8, None, None, FAKE, 8, 0, 8, None, 0, None) == 0
+
+
+def test_matmat_host_workspace_size():
+    # strided blocks ((rows-1)*ld + cols doubles), each rounded up to 256 bytes
+    def r256(b):
+        return (b + 255) // 256 * 256
+    for (lda, ldb, ldc, n1, n2, n3) in ((8, 8, 8, 8, 8, 8), (6, 4, 9, 7, 5, 3),
+                                        (4104, 4104, 4104, 4096, 4096, 4096), (1, 1, 1, 1, 1, 1)):
+        want = (r256(((n1 - 1) * lda + n2) * 8) + r256(((n2 - 1) * ldb + n3) * 8)
+                + r256(((n1 - 1) * ldc + n3) * 8))
+        assert pg.matmat_host_workspace(lda, ldb, ldc, n1, n2, n3) == want
+    assert pg.matmat_host_workspace(5, 5, 5, 0, 5, 5) == 0
+    assert pg.matmat_host_workspace(4, 5, 5, 5, 5, 5) == 0    # lda < N2

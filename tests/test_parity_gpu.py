@@ -473,3 +473,51 @@ def test_storage_beyond_2_31_elements(which, dtype):
     del dA, dB, dC
     torch.cuda.empty_cache()
     assert_bitwise(got, oracle_full(p))
+
+
+# ------------------------------------------- lecture matmat on host memory
+def run_matmat_host(p, pinned=False):
+    """matmat_f64_host on host storage (copies of p's arrays); returns the
+    logical C and the host buffers after the call."""
+    N1, N2, N3 = p.m, p.k, p.n
+    A, B, C = p.A.copy(), p.B.copy(), p.C.copy()
+    if pinned:
+        tA, tB, tC = (torch.from_numpy(x).pin_memory() for x in (A, B, C))
+        A, B, C = tA.numpy(), tB.numpy(), tC.numpy()
+    need = pg.matmat_host_workspace(p.lda, p.ldb, p.ldc, N1, N2, N3)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    pg.matmat_f64_host(p.lda, p.ldb, p.ldc, A, B, C, N1, N2, N3, ws, need)
+    return gi.logical_rowmajor(C, N1, N3, p.ldc).copy(), (A, B, C)
+
+
+@pytest.mark.parametrize("N1,N2,N3,pad", [(1, 1, 1, 0), (37, 53, 29, 8), (300, 257, 129, 3),
+                                          (513, 300, 257, 0), (512, 512, 512, 8),
+                                          (1000, 700, 1300, 1)])
+def test_matmat_host_full_oracle(N1, N2, N3, pad):
+    p = gi.make_rowmajor_problem("mmh", N1, N2, N3, N2 + pad, N3 + pad, N3 + pad, 1.0, 1.0,
+                                 seed=N1 + 2 * N2)
+    C, (A, B, Cbuf) = run_matmat_host(p)
+    assert_f64_parity(C, oracle.matmat_rowmajor_f64(p.lda, p.ldb, p.ldc, p.A, p.B, p.C,
+                                                    N1, N2, N3))
+    # inputs untouched, C's row padding untouched (bit for bit)
+    assert np.array_equal(A.view(np.uint64), p.A.view(np.uint64))
+    assert np.array_equal(B.view(np.uint64), p.B.view(np.uint64))
+    if pad:
+        got_pad = Cbuf.reshape(N1, p.ldc)[:, N3:].view(np.uint64)
+        want_pad = p.C.reshape(N1, p.ldc)[:, N3:].view(np.uint64)
+        assert np.array_equal(got_pad, want_pad)
+
+
+def test_matmat_host_equals_device_path():
+    """Same kernel class on the same values: the host entry's result equals
+    the device entry's bit for bit (exact-integer and random inputs, pinned
+    and pageable host memory)."""
+    for dist, pinned in (("i2", False), ("u", True)):
+        p = gi.make_rowmajor_problem("mmh2", 777, 513, 901, 520, 905, 903, 1.0, 1.0, seed=41,
+                                     dist=dist, c_dist=dist)
+        Ch, _ = run_matmat_host(p, pinned=pinned)
+        Cd = run_matmat(p)
+        assert np.array_equal(Ch.view(np.uint64), Cd.view(np.uint64))
+        if dist == "i2":
+            assert_bitwise(Ch, oracle.matmat_rowmajor_f64(p.lda, p.ldb, p.ldc, p.A, p.B, p.C,
+                                                          p.m, p.k, p.n))
