@@ -169,7 +169,15 @@ struct TileCfg {
   static constexpr int A_STAGE = BK * BM, B_STAGE = BN * BK;  // elements
   static constexpr int A_CHUNKS = A_STAGE / V, B_CHUNKS = B_STAGE / V;
   static constexpr int A_LOADS = A_CHUNKS / NT, B_LOADS = B_CHUNKS / NT;
-  static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * (int)sizeof(T);
+  // Epilogue staging: one region of MB columns x WM rows per wave that
+  // writes C (KS == 2: group 0 only); chunks XOR-swizzled within a column.
+  static constexpr bool STAGED_EPI = sizeof(T) == 4;   // measured: fp64 gains nothing
+  static constexpr int EPI_LDW = WM;
+  static_assert(WM / V >= 8, "epilogue swizzle needs 8 chunks per column");
+  static constexpr int EPI_ELEMS = STAGED_EPI ? WGM * WGN * TR::MB * EPI_LDW : 0;
+  static constexpr int RING_ELEMS = STAGES * (A_STAGE + B_STAGE);
+  static constexpr int LDS_ELEMS = RING_ELEMS > EPI_ELEMS ? RING_ELEMS : EPI_ELEMS;
+  static constexpr int LDS_BYTES = LDS_ELEMS * (int)sizeof(T);
   // 32-bit registers per lane: accumulators, two operand sets, staging.
   static constexpr int ACC_REGS = RB * CB * TR::NACC * (int)sizeof(T) / 4;
   static constexpr int OPS_REGS = (CB * V + V * RB) * (int)sizeof(T) / 4;
@@ -189,8 +197,8 @@ struct TileCfg {
                 "ring pipeline alternates two operand sets per wave's share of a tile");
   static_assert(KS == 1 || (KS == 2 && STAGES > 2), "K split in two, ring pipeline only");
   // K split: group 1's accumulators pass through LDS to group 0 at the end.
-  static_assert(KS == 1 || (WGM * WGN) * RB * CB * TR::NACC * 64 <= STAGES * (A_STAGE + B_STAGE),
-                "K-split hand-over fits in the LDS ring");
+  static_assert(KS == 1 || (WGM * WGN) * RB * CB * TR::NACC * 64 <= LDS_ELEMS,
+                "K-split hand-over fits in LDS");
 };
 
 // f(integral_constant<int, I>) for I = FIRST .. LAST-1, unrolled at compile
@@ -260,7 +268,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
 
   // LDS: the A stages, then the B stages (so that, with a compile-time
   // stage, an access is one per-thread base plus an immediate offset).
-  __shared__ __attribute__((aligned(16))) T lds[STAGES * (Cfg::A_STAGE + Cfg::B_STAGE)];
+  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
 
   // Tile and range of K tiles of this workgroup.
   const int nk_all = (g.K + BK - 1) / BK;
@@ -613,20 +621,19 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
           for (int e = 0; e < TR::NACC; ++e) red[((b * CB + c) * TR::NACC + e) * 64] = acc[b][c][e];
     }
     __syncthreads();
+    if (kgrp == 0) {
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int e = 0; e < TR::NACC; ++e) acc[b][c][e] += red[((b * CB + c) * TR::NACC + e) * 64];
+    }
+    // the epilogue's staging reuses this LDS: every read of it is done first
+    __syncthreads();
     if (kgrp == 1) return;
-#pragma unroll
-    for (int b = 0; b < RB; ++b)
-#pragma unroll
-      for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int e = 0; e < TR::NACC; ++e) acc[b][c][e] += red[((b * CB + c) * TR::NACC + e) * 64];
   }
 
-  // Epilogue.  A lane's accumulator registers come in runs of RUN_R
-  // consecutive block rows (see the trait).  Block b = sb*W + b' puts block
-  // row i at wave-tile row sb*MB*W + W*i + b', so for fixed (c, sb, run) the
-  // lane owns RUN = RUN_R*W consecutive rows of one column: element o of
-  // that run is register run*RUN_R + o/W of block sb*W + o%W.
   // Destination: C, or for a K slice of a split tile its raw partial sums
   // (alpha = 1, beta = 0, all BM x BN elements, column-major with ld = BM)
   // in workspace slot (remainder tile r, slice).
@@ -634,75 +641,158 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   T* const cbase = to_ws ? g.ws + (size_t)(r * g.split + slice) * (BM * BN) : g.C;
   const int ldc = to_ws ? BM : g.ldc;
   const T alpha = to_ws ? T(1) : g.alpha, beta = to_ws ? T(0) : g.beta;
-  const bool full_out = to_ws || full_mn;
-  const int row_off = to_ws ? 0 : m0, col_off = to_ws ? 0 : n0;
+  const bool read_c = beta != T(0);
   constexpr int RUN = TR::RUN_R * W;
   constexpr int NRUN = TR::NACC / TR::RUN_R;
-  constexpr bool VEC_C = (RUN % V == 0);   // whole 16-byte chunks per run
-  const bool read_c = beta != T(0);
+  // A lane's accumulator registers come in runs of RUN_R consecutive block
+  // rows (see the trait).  Block b = sb*W + b' puts block row i at wave-tile
+  // row sb*MB*W + W*i + b', so for fixed (c, sb, run) the lane owns RUN =
+  // RUN_R*W consecutive rows of one column: element o of that run is
+  // register run*RUN_R + o/W of block sb*W + o%W.
+  if constexpr (Cfg::STAGED_EPI) {
+    // Staged through LDS so that global memory sees whole column segments.
+    // Per column block c, each wave writes its MB columns x WM rows to a
+    // private LDS region, then reads it back a 16-byte chunk per lane with
+    // consecutive lanes on consecutive rows: a wave's store covers whole
+    // columns (WM*sizeof(T) bytes each) instead of 16 bytes in each of 32
+    // columns.  Chunk h of column j sits at chunk h ^ (j & 7) of the column's
+    // WM/V chunks: the 8 lanes of a ds_write_b128 cycle (8 consecutive
+    // columns, one chunk index) then hit 8 distinct bank groups, and each read
+    // cycle (8-lane blocks b and b^3) covers 16 distinct groups of a 256-byte
+    // line.  Only this wave touches its region, and a wave's LDS operations
+    // complete in order, so no barrier is needed.
+    const int m_end = to_ws ? BM : M, n_end = to_ws ? BN : N;   // extent in that frame
+    const int row_base = (to_ws ? 0 : m0) + wrow, col_base = (to_ws ? 0 : n0) + wcol;
+    constexpr int LDW = Cfg::EPI_LDW;            // staging column stride (elements)
+    constexpr int CPC = Cfg::WM / V;             // chunks per wave-tile column
+    constexpr int NCH = MB * CPC;                // chunks per column block
+    static_assert(RUN % V == 0, "a run is whole 16-byte chunks");
+    static_assert(NCH % 64 == 0, "whole chunks per lane");
+    T* const stg = lds + wave_in * (MB * LDW);
 #pragma unroll
-  for (int c = 0; c < CB; ++c) {
-    const int col = col_off + wcol + c * MB + lrow;
-    T* pcol = cbase + (size_t)col * ldc;
+    for (int c = 0; c < CB; ++c) {
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      const int row0 = row_off + wrow + sb * MB * W;
-      if (full_out) {
-        // Whole tile in range: issue every C load of this column block
-        // first, then the multiply-adds and stores, so that the loads'
-        // latency is paid once rather than once per run.
-        T cv[NRUN][RUN];
-        if (read_c) {
+      for (int sb = 0; sb < SB; ++sb) {
+#pragma unroll
+        for (int run = 0; run < NRUN; ++run) {
+          T* const pcol = stg + lrow * LDW;
+          const int ch0 = (sb * MB * W + W * TR::irow(run, kslot)) / V;
+#pragma unroll
+          for (int h = 0; h < RUN / V; ++h) {
+            chunk_t v;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+              const int o = h * V + e;
+              v[e] = acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+            }
+            *reinterpret_cast<chunk_t*>(pcol + ((ch0 + h) ^ (lrow & 7)) * V) = v;
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the staging is written
+#pragma unroll
+      for (int i = 0; i < NCH / 64; ++i) {
+        const int q = lane + 64 * i;
+        const int col = q / CPC, rc = q % CPC;
+        const chunk_t v = *reinterpret_cast<const chunk_t*>(stg + col * LDW + (rc ^ (col & 7)) * V);
+        const int gcol = col_base + c * MB + col, grow = row_base + rc * V;
+        if (gcol < n_end) {
+          T* pc = cbase + (size_t)gcol * ldc + grow;
+          if (grow + V <= m_end) {
+            chunk_t out;
+            if (read_c) {
+              const chunk_t cv = load_chunk_full<TR, VEC>(pc);
+#pragma unroll
+              for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cv[e], alpha * v[e]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < V; ++e) out[e] = alpha * v[e];
+            }
+            store_chunk<TR, VEC>(pc, out);
+          } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+              if (grow + e < m_end) {
+                T o = alpha * v[e];
+                if (read_c) o = __builtin_fma(beta, pc[e], o);
+                pc[e] = o;
+              }
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the region is reused
+    }
+  } else {
+    // Direct stores from the accumulator registers: runs of RUN rows of a
+    // column per lane, 16-byte stores where whole chunks.
+    const bool full_out = to_ws || full_mn;
+    const int row_off = to_ws ? 0 : m0, col_off = to_ws ? 0 : n0;
+    constexpr bool VEC_C = (RUN % V == 0);   // whole 16-byte chunks per run
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int col = col_off + wcol + c * MB + lrow;
+      T* pcol = cbase + (size_t)col * ldc;
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const int row0 = row_off + wrow + sb * MB * W;
+        if (full_out) {
+          // Whole tile in range: issue every C load of this column block
+          // first, then the multiply-adds and stores, so that the loads'
+          // latency is paid once rather than once per run.
+          T cv[NRUN][RUN];
+          if (read_c) {
+#pragma unroll
+            for (int run = 0; run < NRUN; ++run) {
+              const T* pc = pcol + row0 + W * TR::irow(run, kslot);
+              if constexpr (VEC_C) {
+#pragma unroll
+                for (int h = 0; h < RUN / V; ++h) {
+                  chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
+#pragma unroll
+                  for (int e = 0; e < V; ++e) cv[run][h * V + e] = v[e];
+                }
+              } else {
+#pragma unroll
+                for (int o = 0; o < RUN; ++o) cv[run][o] = pc[o];
+              }
+            }
+          }
 #pragma unroll
           for (int run = 0; run < NRUN; ++run) {
-            const T* pc = pcol + row0 + W * TR::irow(run, kslot);
+            T* pc = pcol + row0 + W * TR::irow(run, kslot);
+            T out[RUN];
+#pragma unroll
+            for (int o = 0; o < RUN; ++o) {
+              out[o] = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+              if (read_c) out[o] = __builtin_fma(beta, cv[run][o], out[o]);
+            }
             if constexpr (VEC_C) {
 #pragma unroll
               for (int h = 0; h < RUN / V; ++h) {
-                chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
+                chunk_t v;
 #pragma unroll
-                for (int e = 0; e < V; ++e) cv[run][h * V + e] = v[e];
+                for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
+                store_chunk<TR, VEC>(pc + h * V, v);
               }
             } else {
 #pragma unroll
-              for (int o = 0; o < RUN; ++o) cv[run][o] = pc[o];
+              for (int o = 0; o < RUN; ++o) pc[o] = out[o];
             }
           }
-        }
+        } else if (col < N) {
+          // Edge tile: element-wise bounds checks.
 #pragma unroll
-        for (int run = 0; run < NRUN; ++run) {
-          T* pc = pcol + row0 + W * TR::irow(run, kslot);
-          T out[RUN];
+          for (int run = 0; run < NRUN; ++run) {
+            const int row = row0 + W * TR::irow(run, kslot);
+            T* pc = pcol + row;
 #pragma unroll
-          for (int o = 0; o < RUN; ++o) {
-            out[o] = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
-            if (read_c) out[o] = __builtin_fma(beta, cv[run][o], out[o]);
-          }
-          if constexpr (VEC_C) {
-#pragma unroll
-            for (int h = 0; h < RUN / V; ++h) {
-              chunk_t v;
-#pragma unroll
-              for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
-              store_chunk<TR, VEC>(pc + h * V, v);
-            }
-          } else {
-#pragma unroll
-            for (int o = 0; o < RUN; ++o) pc[o] = out[o];
-          }
-        }
-      } else if (col < N) {
-        // Edge tile: element-wise bounds checks.
-#pragma unroll
-        for (int run = 0; run < NRUN; ++run) {
-          const int row = row0 + W * TR::irow(run, kslot);
-          T* pc = pcol + row;
-#pragma unroll
-          for (int o = 0; o < RUN; ++o) {
-            if (row + o < M) {
-              T v = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
-              if (read_c) v = __builtin_fma(beta, pc[o], v);
-              pc[o] = v;
+            for (int o = 0; o < RUN; ++o) {
+              if (row + o < M) {
+                T v = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+                if (read_c) v = __builtin_fma(beta, pc[o], v);
+                pc[o] = v;
+              }
             }
           }
         }

@@ -34,8 +34,6 @@ const Variant<float>* f32_variants(int* count) {
       PGEMM_F32(256, 256, 16, 2, 2, 3, true, vec),     // wave tile 128 x 128
       PGEMM_F32(128, 128, 16, 2, 2, 4, true, vec),     // wave tile 64 x 64
       // plain double buffering (two LDS stages), 4 waves
-      PGEMM_F32(256, 256, 32, 2, 2, 2, true, vec),
-      PGEMM_F32(256, 256, 32, 2, 2, 2, false, ua),
       PGEMM_F32(128, 128, 32, 2, 2, 2, true, vec),
       PGEMM_F32(128, 128, 32, 2, 2, 2, false, ua),
   };
