@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--min-warmup-seconds", type=float, default=0.3,
                     help="keep warming up (untimed) until this much wall time has passed")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the JSON line: every workload once, GPU time, parity "
+                         "against the oracle and the oracle's own time, as a markdown table")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run two device-to-device copies of this many MiB (a plain "
                          "copy of known size, to scale HBM byte counters)")
@@ -169,12 +172,12 @@ def library_digest() -> str:
     return hashlib.sha256(open(LIB, "rb").read()).hexdigest()[:16]
 
 
-def recorded_traffic(variant: str, workload: str):
-    """HBM bytes per launch measured by rocprofv3 counter runs, as recorded in
-    profiles/*counters*.md, or None if none matches this variant, workload
-    and the built library (the kernel changed since it was taken)."""
+def recorded_profile(variant: str, workload: str) -> dict:
+    """Values measured by rocprofv3 counter runs for this variant and
+    workload, as recorded in profiles/*counters*.md, or {} if none matches
+    them and the built library (the kernel changed since they were taken)."""
     if not os.path.isdir(PROFILES):
-        return None
+        return {}
     digest = library_digest()
     for f in sorted(os.listdir(PROFILES)):
         if "counters" not in f:
@@ -185,9 +188,27 @@ def recorded_traffic(variant: str, workload: str):
                 k, v = line[2:].strip().split(": ", 1)
                 kv[k.strip("`")] = v.strip().strip("`")
         if (kv.get("variant") == variant and kv.get("workload") == workload
-                and kv.get("library_digest") == digest and "traffic_bytes_per_launch" in kv):
-            return float(kv["traffic_bytes_per_launch"])
-    return None
+                and kv.get("library_digest") == digest):
+            return kv
+    return {}
+
+
+def recorded_traffic(variant: str, workload: str):
+    """HBM bytes per launch from the recorded counters, or None."""
+    kv = recorded_profile(variant, workload)
+    return float(kv["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in kv else None
+
+
+def recorded_counters(variant: str, workload: str):
+    """MFMA-busy share and LDS bank-conflict cycles from the recorded
+    counters (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE and
+    SQ_LDS_BANK_CONFLICT, per launch), or None."""
+    kv = recorded_profile(variant, workload)
+    if "mfma_util" not in kv or "lds_bank_conflict_cycles" not in kv:
+        return None
+    return {"mfma_util": float(kv["mfma_util"]),
+            "lds_bank_conflict_cycles": float(kv["lds_bank_conflict_cycles"]),
+            "source": "rocprofv3 --pmc, profiles/ (same built library)"}
 
 
 def roofline(r: Resident, kern_ms_mean: float):
@@ -196,6 +217,7 @@ def roofline(r: Resident, kern_ms_mean: float):
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": recorded_traffic(r.variant, r.name),
+            "counters": recorded_counters(r.variant, r.name),
             "algorithmic_bytes": r.algorithmic_bytes(),
             "kernel": r.variant, "kernel_ms_mean": round(kern_ms_mean, 4),
             "entry": r.entry, "workspace_bytes": r.ws_bytes,
@@ -235,6 +257,67 @@ def cpu_baseline(p, first_out: np.ndarray, seconds: float):
                               "ok": bool(maxabs <= 1e-6 * p.k and rel <= 1e-5)}}
 
 
+def sweep(args):
+    """Every workload: GPU kernel time (median of event-timed launches), the
+    parity figures against the oracle (full result up to 4096^3, the first
+    columns at 8192^3) and the oracle's time on the same columns."""
+    import torch
+    import oracle
+    oracle.build(force=False)
+    cores = oracle.num_threads()
+    rows = []
+    for name in gi.WORKLOADS:
+        log("sweep", name)
+        r = Resident(name)
+        p = r.p
+        r.launch()
+        torch.cuda.synchronize()
+        if p.rowmajor:
+            out = r.C.cpu().numpy()
+            got = gi.logical_rowmajor(out, p.m, p.n, p.ldc).astype(np.float64)
+        else:
+            out = r.C.cpu().numpy()
+            got = gi.logical_colmajor(out, p.m, p.n, p.ldc).astype(np.float64)
+        r.reset_c()
+        _, _, kern_med, _ = time_workload(r, max(args.steps, 10), args.warmup,
+                                          args.min_warmup_seconds)
+        cols = p.n if p.m * p.n * p.k <= 4096 ** 3 else 512
+        t0 = time.perf_counter()
+        if p.rowmajor:
+            R = oracle.matmat_rowmajor_f64(p.lda, p.ldb, p.ldc, p.A, p.B, p.C, p.m, p.k, p.n)
+        else:
+            R = oracle.gemm(p.m, cols, p.k, p.alpha, p.A, p.lda, p.B, p.ldb, p.beta, p.C,
+                            p.ldc, dtype=p.dtype)
+        t_or = time.perf_counter() - t0
+        D = got[:, :cols] - R
+        maxabs = float(np.max(np.abs(D)))
+        rel = float(np.linalg.norm(D) / np.linalg.norm(R))
+        if r.dt == "f32":
+            ok = maxabs <= 1e-6 * p.k and rel <= 1e-5
+        else:
+            ok = rel <= 1e-12
+        cnt = recorded_counters(r.variant, r.name)
+        tflops = r.flops / (kern_med * 1e-3) / 1e12
+        rows.append((name, "%dx%dx%d" % (p.m, p.n, p.k), r.entry, r.variant, kern_med, tflops,
+                     100 * tflops / PEAK_TFLOPS[r.dt], cnt, maxabs, rel, ok, t_or, cols, p.n,
+                     2.0 * p.m * cols * p.k / t_or / 1e9))
+        del r
+        torch.cuda.empty_cache()
+    print("| workload | M×N×K | entry, variant | kernel ms (median) | TFLOP/s | %% of peak "
+          "| MfmaUtil | LDS bank conflicts | max\\|ΔC\\| | rel. Frobenius | parity "
+          "| oracle s (%d threads) | oracle GFLOP/s |" % cores)
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for (name, shape, entry, var, ms, tf, pct, cnt, maxabs, rel, ok, t_or, cols, n,
+         ogf) in rows:
+        mu = "%.1f %%" % (100 * cnt["mfma_util"]) if cnt else "—"
+        lc = "%d" % cnt["lds_bank_conflict_cycles"] if cnt else "—"
+        part = "" if cols == n else " (first %d of %d columns)" % (cols, n)
+        print("| %s | %s | `%s`, %s | %.4f | %.1f | %.1f | %s | %s | %.3g | %.3g | %s | %.2f%s "
+              "| %.1f |" % (name, shape, entry, var, ms, tf, pct, mu, lc, maxabs, rel,
+                            "pass" if ok else "FAIL", t_or, part, ogf))
+    sys.stdout.flush()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -246,6 +329,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(args)
+        return
 
     log("generating", args.workload)
     r = Resident(args.workload)

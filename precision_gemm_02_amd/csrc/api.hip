@@ -127,10 +127,12 @@ int device_cus() {
 
 // Split of the last round of tiles.  With T tiles on P compute units, the
 // first R = floor(T/P) rounds stay one tile per workgroup; if the remaining
-// Tr = T - R*P tiles would leave most compute units idle in a last round,
-// each of them is split into s K slices (s*Tr <= P, at least 4 K tiles per
-// slice) whose partial sums go to the workspace and are added, in slice
-// order, by the fix-up kernel.
+// Tr = T - R*P tiles would leave more than half the compute units idle in a
+// last round, each of them is split into s K slices (s*Tr <= P) whose partial
+// sums go to the workspace and are added, in slice order, by the fix-up
+// kernel.  Slices keep at least 4 K tiles after a full round (the split
+// tiles then run beside nothing else) and at least 2 when there is no full
+// round (T < P/2: small problems, where the split is the only parallelism).
 struct SplitPlan {
   int full_tiles = 0, split = 1;
   size_t bytes = 0;
@@ -142,9 +144,10 @@ SplitPlan split_plan(const Variant<T>& v, int m, int n, int k, int cus) {
   const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
   const long long nk = ceil_div(k, v.bk);
-  if (rounds < 1 || rest == 0 || rest * 2 > cus) return p;
+  if (rest == 0 || rest * 2 > cus) return p;
   long long s = cus / rest;
-  if (s > nk / 4) s = nk / 4;
+  const long long min_slice = rounds >= 1 ? 4 : 2;
+  if (s > nk / min_slice) s = nk / min_slice;
   if (s < 2) return p;
   p.full_tiles = (int)(rounds * cus);
   p.split = (int)s;

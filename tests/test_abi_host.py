@@ -171,8 +171,13 @@ def test_workspace_sizes():
     # 256 + 24 leftover tiles, each split into 8 slices of 4 K tiles (32 in
     # all).  256 compute units: the MI355X, and the fallback with no GPU.
     assert pg.workspace_f32(4097, 3001, 1023) == 24 * 8 * 128 * 128 * 4
-    # too few K tiles to split (fewer than 8)
+    # too few K tiles to split after a full round (4 per slice)
     assert pg.workspace_f32(4097, 3001, 100) == 0
+    # fewer tiles than compute units: 1024^3 is 64 tiles of 128^2, each split
+    # into 4 slices (256 / 64) of 8 K tiles
+    assert pg.workspace_f32(1024, 1024, 1024) == 64 * 4 * 128 * 128 * 4
+    # more than half the units busy in the only round: no split
+    assert pg.workspace_f32(1500, 1500, 1500) == 0
 
 
 def test_matmat_host_argument_codes_and_quick_returns():

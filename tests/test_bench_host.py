@@ -46,3 +46,17 @@ def test_recorded_traffic_requires_matching_sources(tmp_path, monkeypatch):
     assert bench.recorded_traffic("v1", "w2") is None
     f.write_text(f.read_text().replace(d, "0" * 16))
     assert bench.recorded_traffic("v1", "w1") is None
+
+
+def test_recorded_counters_require_matching_library(tmp_path, monkeypatch):
+    import bench
+    d = bench.library_digest()
+    f = tmp_path / "y_counters.md"
+    f.write_text("- `variant`: `v1`\n- `workload`: `w1`\n- `library_digest`: `%s`\n"
+                 "- `mfma_util`: `0.9500`\n- `lds_bank_conflict_cycles`: `0`\n" % d)
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    c = bench.recorded_counters("v1", "w1")
+    assert c["mfma_util"] == 0.95 and c["lds_bank_conflict_cycles"] == 0.0
+    assert bench.recorded_traffic("v1", "w1") is None   # not recorded in this file
+    f.write_text(f.read_text().replace(d, "0" * 16))
+    assert bench.recorded_counters("v1", "w1") is None

@@ -388,6 +388,11 @@ SPLIT_SHAPES = [
     (np.float32, 4352, 4096, 640),     # 256^2 tiles: 272 tiles, 10 slices
     (np.float64, 4200, 2048, 300),     # 128^2 fp64 tiles: 528 = 2*256 + 16
     (np.float64, 2100, 2000, 333),     # 128^2 fp64 tiles, K tail
+    # fewer tiles than compute units: every tile split (at least 2 K tiles each)
+    (np.float32, 512, 512, 512),       # 16 tiles x 8 slices
+    (np.float32, 300, 200, 1000),      # 6 edge tiles x 16 slices of 2 K tiles
+    (np.float64, 200, 130, 333),       # 4 edge tiles x 10 slices, K tail
+    (np.float32, 128, 128, 128),       # one tile, 2 slices
 ]
 
 
