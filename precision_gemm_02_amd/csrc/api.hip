@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cstring>
 
 #include "pgemm.h"
@@ -111,18 +112,19 @@ int choose_f64(int m, int n, bool vec) {
 }
 
 // Compute units of the current device (cached per device; 256 if unknown).
+// Threads may race to fill an entry; they all store the same value.
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         v <= 0)
       v = 256;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 // Split of the last round of tiles.  With T tiles on P compute units, the
