@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="sgemm_sweep_8192")
     ap.add_argument("--secondary", nargs="*",
-                    default=["sgemm_2048", "sgemm_ragged", "dgemm_rowmajor"])
+                    default=["sgemm_2048", "sgemm_ragged", "dgemm_rowmajor",
+                             "sgemm_shard_8192_g8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--min-warmup-seconds", type=float, default=0.3,

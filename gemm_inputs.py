@@ -163,6 +163,10 @@ def make_rowmajor_problem(name, N1, N2, N3, lda, ldb, ldc, alpha, beta, seed,
 #                    alpha=0.75, beta=-1.25
 #   dgemm_rowmajor   fp64 row-major 4096^3 with ld 4104, A,B,C U[-1,1) seed 4,
 #                    alpha=1, beta=1 (the lecture's C += A*B)
+#   sgemm_shard_8192_g8
+#                    one GPU's share when sgemm_sweep_8192 is split by columns
+#                    of C over 8 GPUs: the last 1024 columns of B and C (the
+#                    same values, ld 8192), all of A: 8192 x 1024 x 8192
 
 SWEEP_SIZES = (512, 1024, 2048, 4096, 8192)
 
@@ -189,9 +193,18 @@ def workload(name: str, dist_override: Optional[str] = None) -> Problem:
         n = 4096
         return make_rowmajor_problem(name, n, n, n, n + 8, n + 8, n + 8, 1.0, 1.0, 4,
                                      dist=d("u"), c_dist=d("u"))
+    if name == "sgemm_shard_8192_g8":
+        full = workload("sgemm_sweep_8192", dist_override)
+        shards, n = 8, full.n // 8
+        j0 = (shards - 1) * n
+        return Problem(name, np.float32, full.m, n, full.k, full.lda, full.ldb, full.ldc,
+                       full.alpha, full.beta, full.A, full.B[j0 * full.ldb:(j0 + n) * full.ldb],
+                       full.C[j0 * full.ldc:(j0 + n) * full.ldc])
     raise KeyError(name)
 
 
+SHARD_COLUMN0 = {"sgemm_shard_8192_g8": 7 * 1024}   # first column of the shard
+
 WORKLOADS = (["sgemm_128", "sgemm_2048"]
              + ["sgemm_sweep_%d" % n for n in SWEEP_SIZES]
-             + ["sgemm_ragged", "dgemm_rowmajor"])
+             + ["sgemm_ragged", "dgemm_rowmajor", "sgemm_shard_8192_g8"])

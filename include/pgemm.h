@@ -9,9 +9,14 @@
  * Layout.  Column-major, neither operand transposed, as in the SGEMM study
  *   "optimizing-sgemm-on-nvidia-turing-gpus" (introduction).  Element (i, j)
  *   of a matrix X with leading dimension ldx is X[i + j*ldx].  A is m x k,
- *   B is k x n, C is m x n.  Only the logical block is read or written; the
- *   padding rows between the logical extent and the leading dimension are
- *   never read (A, B) and never written (C).
+ *   B is k x n, C is m x n.  Only the logical block of C is written; its
+ *   padding rows (between the logical extent and the leading dimension) are
+ *   never written.  A column of A other than the last may be read up to
+ *   the next 16-byte boundary past row m-1 (whole 16-byte loads at the edge
+ *   of the block; with lda < m rounded up to 16 bytes this reaches the first
+ *   rows of the next column).  Those values never reach C, and every read
+ *   stays inside the (k-1)*lda + m elements of A.  Nothing else outside the
+ *   logical blocks is read.
  * Memory.  A, B, C are DEVICE pointers on the current HIP device, owned by
  *   the caller (matmat_f64_host alone takes host pointers).  The library
  *   allocates nothing per call and keeps no state besides read-only kernel

@@ -301,13 +301,32 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   //  B: column q / KC, inner indices (q % KC)*V .. +V-1 of the tile.
   chunk_t ra[A_LOADS], rb[B_LOADS];
 
-  // Whole tile in range: unmasked loads, no branches.  A thread's chunks
-  // i = 0, 1, ... of a tile lie NT/(BM/V) columns of A (NT/KC columns of B)
-  // apart, so one address per operand is formed up front; chunk i of tile
-  // kt adds a uniform offset, one 64-bit add per load.
+  // Whole K tiles: unmasked loads, no branches.  A thread's chunks i = 0, 1,
+  // ... of a tile lie NT/(BM/V) columns of A apart, so one A address is
+  // formed up front and chunk i of tile kt adds a uniform offset (one 64-bit
+  // add per load); each B chunk keeps its own column address.
+  // Tiles on the M or N edge take the same loads.  An A chunk whose rows
+  // all lie at or beyond M, or a B column at or beyond N, only feeds entries
+  // of C that are never stored, so it is read from row 0 / column 0 instead
+  // (in bounds; the values do not matter).  An A chunk that straddles M (M
+  // not a multiple of V) is read whole: its elements past row M-1 are the
+  // column's padding or, with a tight lda, the first V-2 rows of the next
+  // column, and again only feed rows that are never stored.  Such reads stay
+  // inside the (K-1)*lda + M elements of A when the column is not the last
+  // one and lda >= V-1, so on the M edge the steady state stops before the
+  // last column (k_whole) and the masked loads take the rest.
   static_assert(NT % (BM / V) == 0 && NT % KC == 0, "uniform steps between a thread's chunks");
-  const T* const pa0 = g.A + (size_t)(tid / (BM / V)) * lda + (m0 + (tid % (BM / V)) * V);
-  const T* const pb0 = g.B + (size_t)(n0 + tid / KC) * ldb + (tid % KC) * V;
+  const int a_row = m0 + (tid % (BM / V)) * V;
+  const T* const pa0 = g.A + (size_t)(tid / (BM / V)) * lda + (a_row < M ? a_row : 0);
+  const T* pb0[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int col = n0 + tid / KC + i * (NT / KC);
+    pb0[i] = g.B + (size_t)(col < N ? col : 0) * ldb + (tid % KC) * V;
+  }
+  const bool straddle = (m0 + BM > M) && (M % V != 0);
+  const bool edge_fast = !straddle || lda >= V - 1;
+  const int k_whole = straddle ? (K - 1) / BK : K / BK;   // whole K tiles the loop may load
   auto gload_full = [&](int kt) {
     const size_t astep = (size_t)kt * BK * (size_t)lda;
     const int bstep = kt * BK;
@@ -315,8 +334,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     for (int i = 0; i < A_LOADS; ++i)
       ra[i] = load_chunk_full<TR, VEC>(pa0 + (astep + (size_t)(i * (NT / (BM / V))) * lda));
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      rb[i] = load_chunk_full<TR, VEC>(pb0 + ((size_t)(i * (NT / KC)) * ldb + bstep));
+    for (int i = 0; i < B_LOADS; ++i) rb[i] = load_chunk_full<TR, VEC>(pb0[i] + bstep);
   };
   // Edge tiles and the K tail: out-of-range elements load as zero.
   auto gload_masked = [&](int kt) {
@@ -515,14 +533,14 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     };
     int st = 0;                       // stage of tile kt
     int kt = kt_begin;
-    // Steady state, while tile kt+S exists and is whole (and the tile is
-    // inside C): one branch-free block per iteration.  With in-order issue,
+    // Steady state, while tile kt+S exists and is whole (edge tiles too,
+    // with the redirected loads above): one branch-free block per iteration.  With in-order issue,
     // the next group's operand reads, the tile's LDS stores and its global
     // loads are spread evenly between group 0's MFMAs (each executes while
     // an MFMA occupies the matrix core) instead of running as a block while
     // the matrix core idles.
     const int kt_fast_end =
-        (INTERLEAVE && full_mn) ? max(kt_begin, min(kt_end, K / BK) - S) : kt_begin;
+        (INTERLEAVE && edge_fast) ? max(kt_begin, min(kt_end, k_whole) - S) : kt_begin;
     // The steady state is unrolled by S, so that every stage index is a
     // compile-time constant and each LDS access is a per-thread base plus an
     // immediate offset (no address arithmetic per iteration).

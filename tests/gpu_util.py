@@ -3,8 +3,8 @@
 Every matrix goes to the GPU inside a larger buffer whose margins hold a
 sentinel bit pattern.  After a call the margins, and the leading-dimension
 padding of C, must come back bit-identical: the library must never write
-outside the logical block of C, and must never read padding (A and B padding
-holds NaN, which would poison any result it touched).
+outside the logical block of C, and padding values must never reach C (A and
+B padding holds NaN, which would poison any result it touched).
 """
 from __future__ import annotations
 

@@ -526,3 +526,60 @@ def test_matmat_host_equals_device_path():
         if dist == "i2":
             assert_bitwise(Ch, oracle.matmat_rowmajor_f64(p.lda, p.ldb, p.ldc, p.A, p.B, p.C,
                                                           p.m, p.k, p.n))
+
+
+# ------------------------------------------------ one GPU's share of 8192^3
+def test_column_shard_of_8192_in_place():
+    """The 8-GPU column split of the 8192^3 workload, shard 7, run in place on
+    the full matrices: B and C by pointer offset (B + j0*ldb, C + j0*ldc),
+    all of A.  The shard's entries match the oracle (sampled + two full
+    columns + Freivalds' check), and every column outside it is untouched."""
+    full = gi.workload("sgemm_sweep_8192")
+    p = gi.workload("sgemm_shard_8192_g8")
+    j0 = gi.SHARD_COLUMN0[p.name]
+    dA, dB, dC = DevMat(full.A), DevMat(full.B), DevMat(full.C)
+    item = 4
+    pg.gemm_f32(p.m, p.n, p.k, p.alpha, dA.ptr, p.lda, dB.ptr + j0 * p.ldb * item, p.ldb,
+                p.beta, dC.ptr + j0 * p.ldc * item, p.ldc)
+    torch.cuda.synchronize()
+    store = dC.storage()
+    before = full.C.view(np.uint32)
+    assert np.array_equal(store[:j0 * p.ldc].view(np.uint32), before[:j0 * p.ldc]), \
+        "columns before the shard changed"
+    dC.assert_untouched_outside(full.m, full.n, full.ldc)
+    C = logical(store[j0 * p.ldc:], p.m, p.n, p.ldc).copy()
+    I, J = sample_indices(p.m, p.n, 4096, seed=9)
+    R = oracle.gemm_entries(p.m, p.n, p.k, p.alpha, p.A, p.lda, p.B, p.ldb, p.beta, p.C,
+                            p.ldc, I, J)
+    D = C[I, J].astype(np.float64) - R
+    assert np.max(np.abs(D)) <= 1e-6 * p.k
+    assert np.linalg.norm(D) / np.linalg.norm(R) <= 1e-5
+    for jj in (0, p.n - 1):
+        Rc = oracle.gemm(p.m, 1, p.k, p.alpha, p.A, p.lda, p.B[jj * p.ldb:], p.ldb, p.beta,
+                         p.C[jj * p.ldc:], p.ldc)
+        assert_f32_parity(C[:, jj:jj + 1], Rc, p.k)
+    err = freivalds(C, logical(p.A, p.m, p.k, p.lda), logical(p.B, p.k, p.n, p.ldb),
+                    logical(p.C, p.m, p.n, p.ldc), p.alpha, p.beta, vectors=3)
+    say("shard freivalds rel %.3g" % err)
+    assert err <= 1e-5
+
+
+# ---------------------------- edge tiles with tight leading dimensions
+TIGHT_SHAPES = [(515, 257, 777), (3, 200, 900), (2, 100, 900), (1, 33, 600), (4095, 260, 300),
+                (257, 130, 400)]
+
+
+@pytest.mark.parametrize("variant", [v for v, n in pg.variants().items() if n.endswith("_ua")],
+                         ids=lambda v: pg.variants()[v])
+def test_tight_leading_dimension_edges_exact_integer(variant):
+    """lda = m with m not a multiple of the 16-byte chunk: edge tiles read
+    whole chunks across the end of a column (never in the last column), and
+    tiny m takes the masked loads; C must match the oracle bit for bit."""
+    name = pg.variants()[variant]
+    dtype = np.float32 if name.startswith("f32_") else np.float64
+    for t, (m, n, k) in enumerate(TIGHT_SHAPES):
+        alpha, beta = ALPHA_BETA[t % len(ALPHA_BETA)]
+        p = exact_problem(dtype, m, n, k, alpha, beta, (m, k, m), seed=500 + t)
+        say(name, "tight", (m, n, k))
+        C, _ = run_colmajor(p, variant=variant)
+        assert_bitwise(C, oracle_full(p))
