@@ -156,8 +156,10 @@ const char *pgemm_status_string(int status);
 
 /*
  * Diagnostics.  pgemm_select_f32 / pgemm_select_f64 return the kernel
- * variant id the library would launch for these arguments (host logic only,
- * no HIP call), or a negative status for invalid arguments, or 0 for calls
+ * variant id gemm_f32 / gemm_f64 would launch for these arguments (host
+ * logic only; it may query the current device's compute-unit count, and
+ * without a device assumes 256), or a negative status for invalid
+ * arguments, or 0 for calls
  * that launch no GEMM kernel (quick return or the beta-scaling path).
  * Variant ids are positive; pgemm_variant_name() describes one (NULL if the
  * id is unknown).  gemm_f32_variant / gemm_f64_variant run the GEMM with a

@@ -64,51 +64,44 @@ int find_variant(const Variant<T>* table, int count, const char* name) {
   return 0;
 }
 
-// Variant tables plus the indices the shape/alignment choice uses, looked up
-// by name once.
+// One tile class: the aligned and unaligned variants of one tiling and the
+// share of the matrix-core peak its steady state reaches (measured on the
+// MI355X at 8192^3: 256x256 150.1, 256x128 146.9, 128x128 145.9 TFLOP/s of
+// 157.3).
+struct TileClass {
+  int vec, ua;
+  double eff;
+};
+
+// Variant tables plus the tile classes the shape/alignment choice uses,
+// looked up by name once.
 struct Tables {
   const Variant<float>* f32;
   const Variant<double>* f64;
   int n32, n64;
-  int f32_big_vec, f32_big_ua, f32_small_vec, f32_small_ua;
-  int f64_small_vec, f64_small_ua;
+  TileClass f32c[3];
+  TileClass f64c[1];
   Tables() {
     f32 = f32_variants(&n32);
     f64 = f64_variants(&n64);
-    f32_big_vec = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_vec");
-    f32_big_ua = find_variant(f32, n32, "f32_256x256x16_w2x4_s3_ua");
-    f32_small_vec = find_variant(f32, n32, "f32_128x128x32_w2x2_s3_k2_vec");
-    f32_small_ua = find_variant(f32, n32, "f32_128x128x32_w2x2_s3_k2_ua");
-    f64_small_vec = find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec");
-    f64_small_ua = find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua");
+    f32c[0] = {find_variant(f32, n32, "f32_256x256x16_w2x4_s3_vec"),
+               find_variant(f32, n32, "f32_256x256x16_w2x4_s3_ua"), 0.954};
+    f32c[1] = {find_variant(f32, n32, "f32_256x128x32_w4x2_s3_vec"),
+               find_variant(f32, n32, "f32_256x128x32_w4x2_s3_ua"), 0.934};
+    f32c[2] = {find_variant(f32, n32, "f32_128x128x32_w2x2_s3_k2_vec"),
+               find_variant(f32, n32, "f32_128x128x32_w2x2_s3_k2_ua"), 0.927};
+    // fp64: 128 x 128 tiles at every size.  Their 64 x 32 wave tiles leave
+    // registers for the unrolled steady-state loop, which more than pays for
+    // the extra operand traffic of smaller tiles (4096^3: 74.0 TFLOP/s
+    // against 72.3 for 256 x 128 tiles, whose loop cannot be unrolled).
+    f64c[0] = {find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec"),
+               find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua"), 0.93};
   }
 };
 
 const Tables& tables() {
   static const Tables t;
   return t;
-}
-
-// Variant table index for fp32, by problem shape and alignment.
-//  * 256 x 256 tiles once they give at least one tile per compute unit: the
-//    most reuse per byte loaded.
-//  * 128 x 128 tiles otherwise, so that e.g. 2048^2 still fills all 256 CUs.
-int choose_f32(int m, int n, bool vec) {
-  const Tables& t = tables();
-  const long long t256 = ceil_div(m, 256) * ceil_div(n, 256);
-  if (t256 >= 256) return vec ? t.f32_big_vec : t.f32_big_ua;
-  return vec ? t.f32_small_vec : t.f32_small_ua;
-}
-
-// fp64: 128 x 128 tiles at every size.  Their 64 x 32 wave tiles leave
-// registers for the unrolled steady-state loop, which more than pays for
-// the extra operand traffic of smaller tiles (4096^3 on MI355X: 73.7
-// TFLOP/s against 72.0 for 256 x 128 tiles, whose loop cannot be unrolled).
-int choose_f64(int m, int n, bool vec) {
-  (void)m;
-  (void)n;
-  const Tables& t = tables();
-  return vec ? t.f64_small_vec : t.f64_small_ua;
 }
 
 // Compute units of the current device (cached per device; 256 if unknown).
@@ -155,6 +148,67 @@ SplitPlan split_plan(const Variant<T>& v, int m, int n, int k, int cus) {
   p.split = (int)s;
   p.bytes = (size_t)rest * (size_t)s * (size_t)v.bm * (size_t)v.bn * sizeof(T);
   return p;
+}
+
+// Estimated time of variant v on an m x n x k problem, in multiply-adds of
+// one compute unit at full rate.  Each round of tiles (every compute unit
+// busy with one tile) costs the tile's K loop at the class's efficiency plus
+// a fixed part: ~1.5 us of prologue and the round's stores of C at ~5 TB/s.
+// The last, partly filled round costs a whole round, or with the split of
+// the last round a slice of one plus the fix-up kernel (its HBM traffic at
+// ~4 TB/s and a launch of ~4 us).  Edge tiles cost as much as inner ones
+// (they run the same loop).  On 14 shapes from 1500^3 to 12000 x 2000 x 4000
+// this picks the fastest tile class.
+template <typename T>
+double estimate(const Variant<T>& v, double eff, int m, int n, int k, int cus,
+                bool split_ok) {
+  const double unit_s = 2.0 / (157.3e12 / 256);      // one multiply-add per CU
+  const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
+  const long long rounds = tiles / cus, rest = tiles - rounds * cus;
+  const double c_bytes = (double)cus * v.bm * v.bn * sizeof(T);
+  const double round =
+      (double)v.bm * (double)v.bn * (double)k / eff + (1.5e-6 + c_bytes / 5e12) / unit_s;
+  double t = (double)rounds * round;
+  if (rest == 0) return t;
+  if (split_ok) {
+    const SplitPlan p = split_plan(v, m, n, k, cus);
+    if (p.split > 1) {
+      const double fix_bytes = (double)(p.split + 2) * (double)rest * v.bm * v.bn * sizeof(T);
+      return t + round / p.split + (fix_bytes / 4e12 + 4e-6) / unit_s;
+    }
+  }
+  return t + round;
+}
+
+// Variant table index for this shape and alignment: the tile class with
+// the least estimated time (with the split of the last round if split_ok).
+template <typename T>
+int choose(int m, int n, int k, bool vec, bool split_ok) {
+  const Tables& t = tables();
+  const Variant<T>* table;
+  const TileClass* cls;
+  int ncls;
+  if constexpr (sizeof(T) == 4) {
+    table = t.f32;
+    cls = t.f32c;
+    ncls = 3;
+  } else {
+    table = t.f64;
+    cls = t.f64c;
+    ncls = 1;
+  }
+  const int cus = device_cus();
+  int best = 0;
+  double best_t = 0;
+  for (int c = 0; c < ncls; ++c) {
+    const double e =
+        estimate(table[cls[c].vec], cls[c].eff, m, n, k > 0 ? k : 1, cus, split_ok);
+    if (c == 0 || e < best_t) {
+      best = c;
+      best_t = e;
+    }
+  }
+  return vec ? cls[best].vec : cls[best].ua;
 }
 
 template <typename T>
@@ -208,20 +262,29 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
     return launch_scale(m, n, beta, C, ldc, s) == hipSuccess ? PGEMM_OK : PGEMM_EHIP;
   const bool vec = vec_ok(A, lda, B, ldb, C, ldc);
   const Variant<T>* table;
-  int count, idx;
+  int count;
   if constexpr (sizeof(T) == 4) {
     table = tables().f32;
     count = tables().n32;
-    idx = choose_f32(m, n, vec);
   } else {
     table = tables().f64;
     count = tables().n64;
-    idx = choose_f64(m, n, vec);
   }
+  int idx;
   if (forced >= 0) {
     if (forced >= count) return PGEMM_EVARIANT;
     idx = forced;
     if (table[idx].vec && !vec) return PGEMM_EVARIANT;
+  } else {
+    // with a large enough workspace, the tiling that is best with the split
+    // of the last round; otherwise the best one without it
+    idx = -1;
+    if (ws != nullptr) {
+      const int w = choose<T>(m, n, k, vec, true);
+      const SplitPlan p = split_plan(table[w], m, n, k, device_cus());
+      if (p.split > 1 && ws_bytes >= p.bytes) idx = w;
+    }
+    if (idx < 0) idx = choose<T>(m, n, k, vec, false);
   }
   return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
              static_cast<T*>(ws), ws_bytes, s);
@@ -232,10 +295,10 @@ template <typename T>
 size_t workspace_impl(int m, int n, int k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
   const Tables& t = tables();
-  // the aligned and unaligned variants of a shape class share their tiling
-  if constexpr (sizeof(T) == 4) return split_plan(t.f32[choose_f32(m, n, true)], m, n, k,
-                                                  device_cus()).bytes;
-  else return split_plan(t.f64[choose_f64(m, n, true)], m, n, k, device_cus()).bytes;
+  // the aligned and unaligned variants of a tile class share their tiling
+  const int w = choose<T>(m, n, k, true, true);
+  if constexpr (sizeof(T) == 4) return split_plan(t.f32[w], m, n, k, device_cus()).bytes;
+  else return split_plan(t.f64[w], m, n, k, device_cus()).bytes;
 }
 
 template <typename T>
@@ -245,8 +308,8 @@ int select_impl(int m, int n, int k, T alpha, const T* A, int lda, const T* B, i
   if (st != 0) return st;
   if (m == 0 || n == 0 || k == 0 || alpha == T(0)) return 0;
   const bool vec = vec_ok(A, lda, B, ldb, C, ldc);
-  if constexpr (sizeof(T) == 4) return 1 + choose_f32(m, n, vec);
-  else return 1 + tables().n32 + choose_f64(m, n, vec);
+  if constexpr (sizeof(T) == 4) return 1 + choose<T>(m, n, k, vec, false);
+  else return 1 + tables().n32 + choose<T>(m, n, k, vec, false);
 }
 
 }  // namespace

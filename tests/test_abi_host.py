@@ -176,8 +176,8 @@ def test_workspace_sizes():
     # fewer tiles than compute units: 1024^3 is 64 tiles of 128^2, each split
     # into 4 slices (256 / 64) of 8 K tiles
     assert pg.workspace_f32(1024, 1024, 1024) == 64 * 4 * 128 * 128 * 4
-    # more than half the units busy in the only round: no split
-    assert pg.workspace_f32(1500, 1500, 1500) == 0
+    # every tiling leaves its last round more than half full: no split
+    assert pg.workspace_f32(3840, 3840, 3840) == 0
 
 
 def test_matmat_host_argument_codes_and_quick_returns():

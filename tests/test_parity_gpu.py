@@ -379,13 +379,14 @@ def run_ws(p, ws_bytes=None):
 
 
 # (dtype, m, n, k): each leaves a partly filled last round of tiles on 256
-# compute units and so takes the split path; they cover both tile classes of
+# compute units and so takes the split path; they cover the tile classes of
 # each precision, ragged M/N edges inside the split tiles and a K tail in
 # the last slice.
 SPLIT_SHAPES = [
     (np.float32, 2053, 2048, 1000),    # 128^2 tiles: 272 = 256 + 16, 8 slices
     (np.float32, 2100, 2000, 555),     # 4 slices, K tail of 11
-    (np.float32, 4352, 4096, 640),     # 256^2 tiles: 272 tiles, 10 slices
+    (np.float32, 4352, 4096, 640),     # 128^2 tiles: 1088 = 4*256 + 64, 4 slices
+    (np.float32, 8192, 4352, 640),     # 256^2 tiles: 544 = 2*256 + 32, 8 slices
     (np.float64, 4200, 2048, 300),     # 128^2 fp64 tiles: 528 = 2*256 + 16
     (np.float64, 2100, 2000, 333),     # 128^2 fp64 tiles, K tail
     # fewer tiles than compute units: every tile split (at least 2 K tiles each)
