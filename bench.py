@@ -86,8 +86,6 @@ class Resident:
         else:
             self.args = (p.m, p.n, p.k, p.alpha, self.A.data_ptr(), p.lda, self.B.data_ptr(),
                          p.ldb, p.beta, self.C.data_ptr(), p.ldc)
-        sel = pg.select_f32 if self.dt == "f32" else pg.select_f64
-        self.variant = pg.variants().get(sel(*self.args), "none")
         self.flops = 2.0 * p.m * p.n * p.k
         self.stream = torch.cuda.current_stream()
         # A partly filled last round of tiles is split over K slices when the
@@ -104,6 +102,11 @@ class Resident:
             self.entry = "matmat_f64"
         else:
             self.entry = ("gemm_%s_ws" if self.ws_bytes else "gemm_%s") % self.dt
+        # the kernel the entry point launches, and into how many K slices it
+        # splits the tiles of the last round (1: no split, no fix-up kernel)
+        sel = pg.select_ws_f32 if self.dt == "f32" else pg.select_ws_f64
+        vid, self.split = sel(*self.args, self.ws_bytes)
+        self.variant = pg.variants().get(vid, "none")
 
     def launch(self):
         if self.p.rowmajor:
@@ -220,7 +223,7 @@ def roofline(r: Resident, kern_ms_mean: float):
             "traffic": recorded_traffic(r.variant, r.name),
             "counters": recorded_counters(r.variant, r.name),
             "algorithmic_bytes": r.algorithmic_bytes(),
-            "kernel": r.variant, "kernel_ms_mean": round(kern_ms_mean, 4),
+            "kernel": r.variant, "k_split": r.split, "kernel_ms_mean": round(kern_ms_mean, 4),
             "entry": r.entry, "workspace_bytes": r.ws_bytes,
             "library_digest": library_digest()}
 

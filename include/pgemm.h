@@ -171,6 +171,18 @@ int pgemm_select_f32(int m, int n, int k, float alpha, const float *A, int lda,
                      const float *B, int ldb, float beta, const float *C, int ldc);
 int pgemm_select_f64(int m, int n, int k, double alpha, const double *A, int lda,
                      const double *B, int ldb, double beta, const double *C, int ldc);
+/* The variant gemm_f32_ws / gemm_f64_ws would launch with a workspace of
+ * ws_bytes bytes (0: as without one), same return values as above.  If split
+ * is not NULL it receives the number of K slices each tile of the last,
+ * partly filled round is split into (1: no split; then the call launches
+ * only the GEMM kernel, otherwise also the fix-up kernel that sums the
+ * slices). */
+int pgemm_select_ws_f32(int m, int n, int k, float alpha, const float *A, int lda,
+                        const float *B, int ldb, float beta, const float *C, int ldc,
+                        size_t ws_bytes, int *split);
+int pgemm_select_ws_f64(int m, int n, int k, double alpha, const double *A, int lda,
+                        const double *B, int ldb, double beta, const double *C, int ldc,
+                        size_t ws_bytes, int *split);
 const char *pgemm_variant_name(int variant);
 int pgemm_num_variants(void);
 int gemm_f32_variant(int variant, int m, int n, int k, float alpha, const float *A,

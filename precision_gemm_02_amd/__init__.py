@@ -64,6 +64,8 @@ _lib.gemm_f64_variant.argtypes = [_i] + _lib.gemm_f64.argtypes
 _lib.pgemm_select_f32.argtypes = [_i, _i, _i, _f, _vp, _i, _vp, _i, _f, _vp, _i]
 _lib.pgemm_select_f64.argtypes = [_i, _i, _i, _d, _vp, _i, _vp, _i, _d, _vp, _i]
 _sz = ctypes.c_size_t
+_lib.pgemm_select_ws_f32.argtypes = _lib.pgemm_select_f32.argtypes + [_sz, ctypes.POINTER(_i)]
+_lib.pgemm_select_ws_f64.argtypes = _lib.pgemm_select_f64.argtypes + [_sz, ctypes.POINTER(_i)]
 _lib.gemm_f32_ws.argtypes = _lib.gemm_f32.argtypes[:11] + [_vp, _sz, _vp]
 _lib.gemm_f64_ws.argtypes = _lib.gemm_f64.argtypes[:11] + [_vp, _sz, _vp]
 _lib.pgemm_workspace_f32.argtypes = [_i, _i, _i]
@@ -80,7 +82,7 @@ _lib.pgemm_variant_name.argtypes = [_i]
 _lib.pgemm_variant_name.restype = ctypes.c_char_p
 for _name in ("gemm_f32", "gemm_f64", "matmat_f64", "gemm_f32_variant", "gemm_f64_variant",
               "pgemm_select_f32", "pgemm_select_f64", "pgemm_num_variants", "gemm_f32_ws",
-              "gemm_f64_ws"):
+              "gemm_f64_ws", "pgemm_select_ws_f32", "pgemm_select_ws_f64"):
     getattr(_lib, _name).restype = _i
 
 PGEMM_OK = 0
@@ -91,7 +93,8 @@ EXPORTS = ("gemm_f32", "gemm_f64", "matmat_f64", "pgemm_status_string",
            "pgemm_select_f32", "pgemm_select_f64", "pgemm_variant_name",
            "pgemm_num_variants", "gemm_f32_variant", "gemm_f64_variant",
            "gemm_f32_ws", "gemm_f64_ws", "pgemm_workspace_f32", "pgemm_workspace_f64",
-           "matmat_f64_host", "pgemm_matmat_host_workspace")
+           "matmat_f64_host", "pgemm_matmat_host_workspace", "pgemm_select_ws_f32",
+           "pgemm_select_ws_f64")
 
 
 class PgemmError(RuntimeError):
@@ -212,6 +215,22 @@ def select_f32(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
 def select_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
     return _lib.pgemm_select_f64(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
                                  _addr(C), ldc)
+
+
+def select_ws_f32(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws_bytes):
+    """(variant id, K slices of the split tiles) gemm_f32_ws would use."""
+    split = ctypes.c_int(1)
+    v = _lib.pgemm_select_ws_f32(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                 _addr(C), ldc, ws_bytes, ctypes.byref(split))
+    return v, split.value
+
+
+def select_ws_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws_bytes):
+    """(variant id, K slices of the split tiles) gemm_f64_ws would use."""
+    split = ctypes.c_int(1)
+    v = _lib.pgemm_select_ws_f64(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                 _addr(C), ldc, ws_bytes, ctypes.byref(split))
+    return v, split.value
 
 
 def variants():

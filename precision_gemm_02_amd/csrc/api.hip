@@ -211,6 +211,27 @@ int choose(int m, int n, int k, bool vec, bool split_ok) {
   return vec ? cls[best].vec : cls[best].ua;
 }
 
+// The variant a call launches: with a workspace large enough for its split
+// plan, the tiling that is best with the split of the last round; otherwise
+// the best one without it.  *split (if given) receives the number of K slices
+// of the split tiles, 1 when there is no split.
+template <typename T>
+int pick(int m, int n, int k, bool vec, size_t ws_bytes, int* split) {
+  const Variant<T>* table;
+  if constexpr (sizeof(T) == 4) table = tables().f32;
+  else table = tables().f64;
+  if (split != nullptr) *split = 1;
+  if (ws_bytes > 0) {
+    const int w = choose<T>(m, n, k, vec, true);
+    const SplitPlan p = split_plan(table[w], m, n, k, device_cus());
+    if (p.split > 1 && ws_bytes >= p.bytes) {
+      if (split != nullptr) *split = p.split;
+      return w;
+    }
+  }
+  return choose<T>(m, n, k, vec, false);
+}
+
 template <typename T>
 hipError_t launch_scale(int m, int n, T beta, T* C, int ldc, hipStream_t s) {
   if (beta == T(1)) return hipSuccess;
@@ -276,15 +297,7 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
     idx = forced;
     if (table[idx].vec && !vec) return PGEMM_EVARIANT;
   } else {
-    // with a large enough workspace, the tiling that is best with the split
-    // of the last round; otherwise the best one without it
-    idx = -1;
-    if (ws != nullptr) {
-      const int w = choose<T>(m, n, k, vec, true);
-      const SplitPlan p = split_plan(table[w], m, n, k, device_cus());
-      if (p.split > 1 && ws_bytes >= p.bytes) idx = w;
-    }
-    if (idx < 0) idx = choose<T>(m, n, k, vec, false);
+    idx = pick<T>(m, n, k, vec, ws != nullptr ? ws_bytes : 0, nullptr);
   }
   return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
              static_cast<T*>(ws), ws_bytes, s);
@@ -303,13 +316,15 @@ size_t workspace_impl(int m, int n, int k) {
 
 template <typename T>
 int select_impl(int m, int n, int k, T alpha, const T* A, int lda, const T* B, int ldb,
-                const T* C, int ldc) {
+                const T* C, int ldc, size_t ws_bytes, int* split) {
+  if (split != nullptr) *split = 1;
   const int st = check_args(m, n, k, alpha, A, lda, B, ldb, C, ldc);
   if (st != 0) return st;
   if (m == 0 || n == 0 || k == 0 || alpha == T(0)) return 0;
   const bool vec = vec_ok(A, lda, B, ldb, C, ldc);
-  if constexpr (sizeof(T) == 4) return 1 + choose<T>(m, n, k, vec, false);
-  else return 1 + tables().n32 + choose<T>(m, n, k, vec, false);
+  const int idx = pick<T>(m, n, k, vec, ws_bytes, split);
+  if constexpr (sizeof(T) == 4) return 1 + idx;
+  else return 1 + tables().n32 + idx;
 }
 
 }  // namespace
@@ -440,13 +455,27 @@ const char* pgemm_status_string(int status) {
 int pgemm_select_f32(int m, int n, int k, float alpha, const float* A, int lda,
                      const float* B, int ldb, float beta, const float* C, int ldc) {
   (void)beta;
-  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc);
+  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc, 0, nullptr);
 }
 
 int pgemm_select_f64(int m, int n, int k, double alpha, const double* A, int lda,
                      const double* B, int ldb, double beta, const double* C, int ldc) {
   (void)beta;
-  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc);
+  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc, 0, nullptr);
+}
+
+int pgemm_select_ws_f32(int m, int n, int k, float alpha, const float* A, int lda,
+                        const float* B, int ldb, float beta, const float* C, int ldc,
+                        size_t ws_bytes, int* split) {
+  (void)beta;
+  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, split);
+}
+
+int pgemm_select_ws_f64(int m, int n, int k, double alpha, const double* A, int lda,
+                        const double* B, int ldb, double beta, const double* C, int ldc,
+                        size_t ws_bytes, int* split) {
+  (void)beta;
+  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, split);
 }
 
 int pgemm_num_variants(void) { return tables().n32 + tables().n64; }

@@ -137,6 +137,27 @@ def test_selection_by_shape_and_alignment():
     assert name_of(v).endswith("_ua")
 
 
+def test_selection_with_workspace():
+    # the ragged 4097 x 3001 x 1023 problem: with the workspace it asks for,
+    # 128 x 128 tiles with the 24 leftover tiles split into 8 K slices;
+    # without it, the plain choice (no split)
+    args = (4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
+    ws = pg.workspace_f32(*args[:3])
+    v, split = pg.select_ws_f32(*args, ws)
+    assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_ua") and split == 8
+    for short in (0, ws - 1):
+        v0, split0 = pg.select_ws_f32(*args, short)
+        assert v0 == pg.select_f32(*args) and split0 == 1
+    # shapes that fill whole rounds: same as the plain entry point
+    sq = (8192, 8192, 8192, 1.5, FAKE, 8192, FAKE, 8192, 0.5, FAKE, 8192)
+    assert pg.select_ws_f32(*sq, 1 << 30) == (pg.select_f32(*sq), 1)
+    d = (4096, 4096, 4096, 1.0, FAKE, 4104, FAKE, 4104, 1.0, FAKE, 4104)
+    assert pg.select_ws_f64(*d, 1 << 30) == (pg.select_f64(*d), 1)
+    # invalid arguments: the same status as the plain selector, split left at 1
+    bad = (4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4)
+    assert pg.select_ws_f32(*bad, 1 << 20) == (-6, 1)
+
+
 def test_status_strings():
     assert pg.status_string(0) == "success"
     assert "launch" in pg.status_string(pg.PGEMM_EHIP)
