@@ -104,6 +104,10 @@ struct GemmArgs {
   int full_tiles;
   int split;
   T* ws;
+  // Nonzero when every offset of a whole-tile load from its tile's first
+  // row/column fits a signed 32-bit byte count (see buffer_offsets_fit);
+  // otherwise all tiles take the masked loads, with 64-bit addresses.
+  int buf32;
 };
 
 // Workgroup id -> linear tile id, for `count` workgroups.  The dispatcher
@@ -253,6 +257,35 @@ __device__ __forceinline__ typename TR::chunk_t load_chunk(const typename TR::T*
   return v;
 }
 
+// Whole-tile loads go through a buffer resource (a scalar descriptor whose
+// base is the tile's first element in the current K tile) with a 32-bit
+// per-lane byte offset that stays the same for every K tile and a scalar
+// offset per chunk.  The loop then spends no vector instructions on
+// addresses and keeps no 64-bit pointers in registers.  Range checking is
+// off (the record count is the maximum); every address is in bounds by
+// construction.  The word-3 value selects 32-bit data for gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <class TR>
+__device__ __forceinline__ typename TR::chunk_t load_chunk_buf(__amdgpu_buffer_rsrc_t r,
+                                                               int voff, int soff) {
+  return __builtin_bit_cast(typename TR::chunk_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, kBufferWord3);
+}
+
+// Host check for GemmArgs::buf32: the largest byte offset of a whole-tile
+// load from its descriptor base is below BK*lda + BM elements (A) and
+// BN*ldb + BK elements (B).
+template <typename T>
+__host__ inline bool buffer_offsets_fit(int bm, int bn, int bk, long long lda, long long ldb) {
+  const long long lim = 0x7fffffffLL / (long long)sizeof(T);
+  return bk * lda + bm < lim && bn * ldb + bk < lim;
+}
+
 // ---------------------------------------------------------------- kernel
 template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS>
 __global__ void __launch_bounds__(WGM * WGN * 64 * KS)
@@ -301,14 +334,14 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   //  B: column q / KC, inner indices (q % KC)*V .. +V-1 of the tile.
   chunk_t ra[A_LOADS], rb[B_LOADS];
 
-  // Whole K tiles: unmasked loads, no branches.  A thread's chunks i = 0, 1,
-  // ... of a tile lie NT/(BM/V) columns of A apart, so one A address is
-  // formed up front and chunk i of tile kt adds a uniform offset (one 64-bit
-  // add per load); each B chunk keeps its own column address.
+  // Whole K tiles: unmasked buffer loads, no branches.  A thread's chunks
+  // i = 0, 1, ... of a tile lie NT/(BM/V) columns of A apart, so A needs one
+  // per-lane offset and a scalar step per chunk; each B chunk keeps its own
+  // per-lane offset.  The descriptors move by whole K tiles (scalar work).
   // Tiles on the M or N edge take the same loads.  An A chunk whose rows
   // all lie at or beyond M, or a B column at or beyond N, only feeds entries
-  // of C that are never stored, so it is read from row 0 / column 0 instead
-  // (in bounds; the values do not matter).  An A chunk that straddles M (M
+  // of C that are never stored, so it is read from the tile's first row /
+  // column instead (in bounds; the values do not matter).  An A chunk that straddles M (M
   // not a multiple of V) is read whole: its elements past row M-1 are the
   // column's padding or, with a tight lda, the first V-2 rows of the next
   // column, and again only feed rows that are never stored.  Such reads stay
@@ -316,25 +349,35 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   // one and lda >= V-1, so on the M edge the steady state stops before the
   // last column (k_whole) and the masked loads take the rest.
   static_assert(NT % (BM / V) == 0 && NT % KC == 0, "uniform steps between a thread's chunks");
+  // Byte offsets from the tile's first row (A, in the tile's K tile) and
+  // first column (B): A chunk i of tile kt is at a_off + i*a_step from
+  // A + m0 + kt*BK*lda, B chunk i at b_off[i] from B + n0*ldb + kt*BK.
+  // (Formed in 64 bits; they fit 32 when g.buf32 is set, and are unused
+  // otherwise.)
   const int a_row = m0 + (tid % (BM / V)) * V;
-  const T* const pa0 = g.A + (size_t)(tid / (BM / V)) * lda + (a_row < M ? a_row : 0);
-  const T* pb0[B_LOADS];
+  constexpr long long TS = sizeof(T);
+  const int a_off =
+      (int)(((long long)(tid / (BM / V)) * lda + (a_row < M ? a_row - m0 : 0)) * TS);
+  constexpr int A_COLS = NT / (BM / V);   // columns of A between a thread's chunks
+  const int a_step = (int)((long long)A_COLS * lda * TS);
+  int b_off[B_LOADS];
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
-    const int col = n0 + tid / KC + i * (NT / KC);
-    pb0[i] = g.B + (size_t)(col < N ? col : 0) * ldb + (tid % KC) * V;
+    const int nn = tid / KC + i * (NT / KC);
+    b_off[i] = (int)(((long long)(n0 + nn < N ? nn : 0) * ldb + (tid % KC) * V) * TS);
   }
+  const T* const a_tile = g.A + m0;
+  const T* const b_tile = g.B + (size_t)n0 * ldb;
   const bool straddle = (m0 + BM > M) && (M % V != 0);
   const bool edge_fast = !straddle || lda >= V - 1;
   const int k_whole = straddle ? (K - 1) / BK : K / BK;   // whole K tiles the loop may load
   auto gload_full = [&](int kt) {
-    const size_t astep = (size_t)kt * BK * (size_t)lda;
-    const int bstep = kt * BK;
+    const __amdgpu_buffer_rsrc_t ar = tile_rsrc(a_tile + (size_t)kt * BK * (size_t)lda);
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      ra[i] = load_chunk_full<TR, VEC>(pa0 + (astep + (size_t)(i * (NT / (BM / V))) * lda));
+    for (int i = 0; i < A_LOADS; ++i) ra[i] = load_chunk_buf<TR>(ar, a_off, i * a_step);
+    const __amdgpu_buffer_rsrc_t br = tile_rsrc(b_tile + (size_t)kt * BK);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) rb[i] = load_chunk_full<TR, VEC>(pb0[i] + bstep);
+    for (int i = 0; i < B_LOADS; ++i) rb[i] = load_chunk_buf<TR>(br, b_off[i], 0);
   };
   // Edge tiles and the K tail: out-of-range elements load as zero.
   auto gload_masked = [&](int kt) {
@@ -359,7 +402,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     }
   };
   auto gload = [&](int kt) {
-    if (full_mn && (kt + 1) * BK <= K) gload_full(kt);
+    if (g.buf32 && full_mn && (kt + 1) * BK <= K) gload_full(kt);
     else gload_masked(kt);
   };
 
@@ -539,8 +582,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // loads are spread evenly between group 0's MFMAs (each executes while
     // an MFMA occupies the matrix core) instead of running as a block while
     // the matrix core idles.
-    const int kt_fast_end =
-        (INTERLEAVE && edge_fast) ? max(kt_begin, min(kt_end, k_whole) - S) : kt_begin;
+    const int kt_fast_end = (INTERLEAVE && edge_fast && g.buf32)
+                                ? max(kt_begin, min(kt_end, k_whole) - S)
+                                : kt_begin;
     // The steady state is unrolled by S, so that every stage index is a
     // compile-time constant and each LDS access is a per-thread base plus an
     // immediate offset (no address arithmetic per iteration).

@@ -35,6 +35,7 @@ hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
     g.split = 1;
   }
   const int rest = tiles - g.full_tiles;
+  g.buf32 = buffer_offsets_fit<T>(BM, BN, BK, g.lda, g.ldb) ? 1 : 0;
   void* args[] = {&g};
   const dim3 grid((unsigned)(g.full_tiles + rest * g.split)), block(WGM * WGN * 64 * KS);
   hipError_t e = hipLaunchKernel(

@@ -481,6 +481,46 @@ def test_storage_beyond_2_31_elements(which, dtype):
     assert_bitwise(got, oracle_full(p))
 
 
+BUFFER_LIMIT_CASES = [
+    # (variant, ldb): 256-column tiles reach BN*ldb + BK elements past the
+    # tile's first column; 2^21 columns of fp32 cross 2^31 bytes (64-bit
+    # masked loads), 2^21 - 64 stays just below (32-bit buffer offsets)
+    ("f32_256x256x16_w2x4_s3_vec", 1 << 21), ("f32_256x256x16_w2x4_s3_vec", (1 << 21) - 64),
+    ("f32_256x256x16_w2x4_s3_ua", (1 << 21) + 1), ("f32_256x256x16_w2x4_s3_ua", (1 << 21) - 63),
+    ("f64_128x128x16_w2x4_s3_vec", 1 << 21), ("f64_128x128x16_w2x4_s3_vec", (1 << 21) - 32),
+]
+
+
+@pytest.mark.parametrize("name,ldb", BUFFER_LIMIT_CASES, ids=lambda x: str(x))
+def test_whole_tile_loads_at_the_32_bit_offset_limit(name, ldb):
+    """Whole-tile loads address each operand from its tile's first row or
+    column with 32-bit byte offsets; when a leading dimension would take
+    them past 2^31 bytes the kernel loads every tile with 64-bit masked
+    addresses instead.  Both sides of the limit, edge tiles and a K tail."""
+    dtype = np.float32 if name.startswith("f32_") else np.float64
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    variant = [v for v, nm in pg.variants().items() if nm == name][0]
+    m, n, k = 300, 260, 40
+    lda, ldc = m + 1, m + 3
+    if name.endswith("_vec"):
+        lda, ldc = 304, 304
+    p = exact_problem(dtype, m, n, k, 1.5, 0.5, (m, k, m), seed=450)
+    A = logical(p.A, m, k, m)
+    B = logical(p.B, k, n, k)
+    C0 = logical(p.C, m, n, m)
+    say("buffer limit", name, "ldb", ldb)
+    dA = _big_storage(A, m, k, lda, tdt)
+    dB = _big_storage(B, k, n, ldb, tdt)
+    dC = _big_storage(C0, m, n, ldc, tdt)
+    fn = pg.gemm_f32_variant if dtype == np.float32 else pg.gemm_f64_variant
+    fn(variant, m, n, k, p.alpha, dA, lda, dB, ldb, p.beta, dC, ldc)
+    torch.cuda.synchronize()
+    got = dC.view(n, ldc)[:, :m].t().cpu().numpy()
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    assert_bitwise(got, oracle_full(p))
+
+
 # ------------------------------------------- lecture matmat on host memory
 def run_matmat_host(p, pinned=False):
     """matmat_f64_host on host storage (copies of p's arrays); returns the
