@@ -731,6 +731,23 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     static_assert(RUN % V == 0, "a run is whole 16-byte chunks");
     static_assert(NCH % 64 == 0, "whole chunks per lane");
     T* const stg = lds + wave_in * (MB * LDW);
+    // With beta != 0 and the whole tile inside C, the old C of column block
+    // c+1 is loaded as soon as block c is staged (its accumulators are free
+    // then), so that its HBM latency passes while block c is stored; block
+    // 0's loads go out before its staging.
+    constexpr int NI = NCH / 64;                 // chunks per lane per column block
+    const bool pre_c = read_c && !to_ws && full_mn;
+    chunk_t cpre[2][NI];
+    auto load_c_block = [&](int c, chunk_t (&dst)[NI]) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int q = lane + 64 * i;
+        const int col = q / CPC, rc = q % CPC;
+        dst[i] = load_chunk_full<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc +
+                                          (row_base + rc * V));
+      }
+    };
+    if (pre_c) load_c_block(0, cpre[0]);
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
 #pragma unroll
@@ -752,6 +769,23 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the staging is written
+      if (pre_c) {
+        if (c + 1 < CB) load_c_block(c + 1, cpre[(c + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int q = lane + 64 * i;
+          const int col = q / CPC, rc = q % CPC;
+          const chunk_t v =
+              *reinterpret_cast<const chunk_t*>(stg + col * LDW + (rc ^ (col & 7)) * V);
+          chunk_t out;
+#pragma unroll
+          for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cpre[c & 1][i][e], alpha * v[e]);
+          store_chunk<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc + (row_base + rc * V),
+                               out);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the region is reused
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < NCH / 64; ++i) {
         const int q = lane + 64 * i;
@@ -791,6 +825,63 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     const bool full_out = to_ws || full_mn;
     const int row_off = to_ws ? 0 : m0, col_off = to_ws ? 0 : n0;
     constexpr bool VEC_C = (RUN % V == 0);   // whole 16-byte chunks per run
+    // The old C of group (c, sb): NRUN runs of RUN rows of this lane's column.
+    auto load_c_group = [&](int c, int sb, T (&cv)[NRUN][RUN]) {
+      const T* pcol = cbase + (size_t)(col_off + wcol + c * MB + lrow) * ldc;
+      const int row0 = row_off + wrow + sb * MB * W;
+#pragma unroll
+      for (int run = 0; run < NRUN; ++run) {
+        const T* pc = pcol + row0 + W * TR::irow(run, kslot);
+        if constexpr (VEC_C) {
+#pragma unroll
+          for (int h = 0; h < RUN / V; ++h) {
+            chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
+#pragma unroll
+            for (int e = 0; e < V; ++e) cv[run][h * V + e] = v[e];
+          }
+        } else {
+#pragma unroll
+          for (int o = 0; o < RUN; ++o) cv[run][o] = pc[o];
+        }
+      }
+    };
+    if (read_c && full_mn && !to_ws) {
+      // Whole tile inside C with beta != 0: the old C of the next group is
+      // loaded before this group's multiply-adds and stores, so that one
+      // HBM latency is exposed per tile instead of one per group.
+      constexpr int NG_EPI = CB * SB;
+      T cvb[2][NRUN][RUN];
+      load_c_group(0, 0, cvb[0]);
+#pragma unroll
+      for (int gq = 0; gq < NG_EPI; ++gq) {
+        const int c = gq / SB, sb = gq % SB;
+        if (gq + 1 < NG_EPI) load_c_group((gq + 1) / SB, (gq + 1) % SB, cvb[(gq + 1) & 1]);
+        T* pcol = cbase + (size_t)(col_off + wcol + c * MB + lrow) * ldc;
+        const int row0 = row_off + wrow + sb * MB * W;
+#pragma unroll
+        for (int run = 0; run < NRUN; ++run) {
+          T* pc = pcol + row0 + W * TR::irow(run, kslot);
+          T out[RUN];
+#pragma unroll
+          for (int o = 0; o < RUN; ++o)
+            out[o] = __builtin_fma(beta, cvb[gq & 1][run][o],
+                                   alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W]);
+          if constexpr (VEC_C) {
+#pragma unroll
+            for (int h = 0; h < RUN / V; ++h) {
+              chunk_t v;
+#pragma unroll
+              for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
+              store_chunk<TR, VEC>(pc + h * V, v);
+            }
+          } else {
+#pragma unroll
+            for (int o = 0; o < RUN; ++o) pc[o] = out[o];
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       const int col = col_off + wcol + c * MB + lrow;
@@ -803,23 +894,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
           // first, then the multiply-adds and stores, so that the loads'
           // latency is paid once rather than once per run.
           T cv[NRUN][RUN];
-          if (read_c) {
-#pragma unroll
-            for (int run = 0; run < NRUN; ++run) {
-              const T* pc = pcol + row0 + W * TR::irow(run, kslot);
-              if constexpr (VEC_C) {
-#pragma unroll
-                for (int h = 0; h < RUN / V; ++h) {
-                  chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
-#pragma unroll
-                  for (int e = 0; e < V; ++e) cv[run][h * V + e] = v[e];
-                }
-              } else {
-#pragma unroll
-                for (int o = 0; o < RUN; ++o) cv[run][o] = pc[o];
-              }
-            }
-          }
+          if (read_c) load_c_group(c, sb, cv);
 #pragma unroll
           for (int run = 0; run < NRUN; ++run) {
             T* pc = pcol + row0 + W * TR::irow(run, kslot);
