@@ -66,8 +66,8 @@ int find_variant(const Variant<T>* table, int count, const char* name) {
 
 // One tile class: the aligned and unaligned variants of one tiling and the
 // share of the matrix-core peak its steady state reaches (measured on the
-// MI355X at 8192^3: 256x256 150.1, 256x128 146.9, 128x128 145.9 TFLOP/s of
-// 157.3).
+// MI355X, one round of 256 tiles timed against K: 256x256 154.4, 128x128
+// 153.4, 256x128 152.6 TFLOP/s of 157.3; fp64 128x128 76.9 of 78.6).
 struct TileClass {
   int vec, ua;
   double eff;
@@ -85,17 +85,21 @@ struct Tables {
     f32 = f32_variants(&n32);
     f64 = f64_variants(&n64);
     f32c[0] = {find_variant(f32, n32, "f32_256x256x16_w2x4_s3_vec"),
-               find_variant(f32, n32, "f32_256x256x16_w2x4_s3_ua"), 0.954};
+               find_variant(f32, n32, "f32_256x256x16_w2x4_s3_ua"), 0.982};
     f32c[1] = {find_variant(f32, n32, "f32_256x128x32_w4x2_s3_vec"),
-               find_variant(f32, n32, "f32_256x128x32_w4x2_s3_ua"), 0.934};
-    f32c[2] = {find_variant(f32, n32, "f32_128x128x32_w2x2_s3_k2_vec"),
-               find_variant(f32, n32, "f32_128x128x32_w2x2_s3_k2_ua"), 0.927};
+               find_variant(f32, n32, "f32_256x128x32_w4x2_s3_ua"), 0.970};
+    // 128 x 128: a ring of 4 stages of BK 16 and 8 waves of 32 x 64; it has
+    // the least fixed cost per tile of the 128 x 128 configurations (no
+    // hand-over between K groups), which is what decides at these sizes
+    // (2048^3 144.5 against 143.2 TFLOP/s for two K groups of 4 waves).
+    f32c[2] = {find_variant(f32, n32, "f32_128x128x16_w4x2_s4_vec"),
+               find_variant(f32, n32, "f32_128x128x16_w4x2_s4_ua"), 0.975};
     // fp64: 128 x 128 tiles at every size.  Their 64 x 32 wave tiles leave
     // registers for the unrolled steady-state loop, which more than pays for
     // the extra operand traffic of smaller tiles (4096^3: 74.0 TFLOP/s
     // against 72.3 for 256 x 128 tiles, whose loop cannot be unrolled).
     f64c[0] = {find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec"),
-               find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua"), 0.93};
+               find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua"), 0.978};
   }
 };
 

@@ -139,12 +139,12 @@ def test_selection_by_shape_and_alignment():
 
 def test_selection_with_workspace():
     # the ragged 4097 x 3001 x 1023 problem: with the workspace it asks for,
-    # 128 x 128 tiles with the 24 leftover tiles split into 8 K slices;
+    # 128 x 128 tiles with the 24 leftover tiles split into 10 K slices;
     # without it, the plain choice (no split)
     args = (4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
     ws = pg.workspace_f32(*args[:3])
     v, split = pg.select_ws_f32(*args, ws)
-    assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_ua") and split == 8
+    assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_ua") and split == 10
     for short in (0, ws - 1):
         v0, split0 = pg.select_ws_f32(*args, short)
         assert v0 == pg.select_f32(*args) and split0 == 1
@@ -188,10 +188,11 @@ def test_workspace_sizes():
     assert pg.workspace_f32(8192, 8192, 8192) == 0
     assert pg.workspace_f32(2048, 2048, 2048) == 0
     assert pg.workspace_f32(0, 10, 10) == 0 and pg.workspace_f32(10, 10, 0) == 0
-    # 4097 x 3001 x 1023 on 128 x 128 tiles: 33 x 24 = 792 tiles = 3 rounds of
-    # 256 + 24 leftover tiles, each split into 8 slices of 4 K tiles (32 in
-    # all).  256 compute units: the MI355X, and the fallback with no GPU.
-    assert pg.workspace_f32(4097, 3001, 1023) == 24 * 8 * 128 * 128 * 4
+    # 4097 x 3001 x 1023 on 128 x 128 x 16 tiles: 33 x 24 = 792 tiles = 3
+    # rounds of 256 + 24 leftover tiles, each split into min(256 // 24, 64 // 4)
+    # = 10 slices of 6 or 7 K tiles (64 in all).  256 compute units: the
+    # MI355X, and the fallback with no GPU.
+    assert pg.workspace_f32(4097, 3001, 1023) == 24 * 10 * 128 * 128 * 4
     # too few K tiles to split after a full round (4 per slice)
     assert pg.workspace_f32(4097, 3001, 100) == 0
     # fewer tiles than compute units: 1024^3 is 64 tiles of 128^2, each split
