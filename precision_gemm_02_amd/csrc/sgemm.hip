@@ -22,17 +22,19 @@ const Variant<float>* f32_variants(int* count) {
       // LDS ring of 3, 8 waves (2 per SIMD), wave tile 128 x 64: large problems
       PGEMM_F32(256, 256, 16, 2, 4, 3, true, vec),
       PGEMM_F32(256, 256, 16, 2, 4, 3, false, ua),
-      // 256 x 128 tiles, 8 waves of 64 x 64: one round of 256 tiles for
-      // 4096 x 2048 shares such as one GPU's 1024 columns of 8192^2
+      // 256 x 128 tiles, 8 waves of 64 x 64: shapes where whole rounds of
+      // these tiles beat both neighbours
       PGEMM_F32(256, 128, 32, 4, 2, 3, true, vec),
       PGEMM_F32(256, 128, 32, 4, 2, 3, false, ua),
       // 128 x 128 tiles fill 256 CUs from 2048^2: K split over two groups
-      // of 4 waves with 64 x 64 wave tiles (default), or 8 waves of 32 x 64
+      // of 4 waves with 64 x 64 wave tiles, 8 waves of 32 x 64 with BK 32,
+      // or (the 128 x 128 class: least fixed cost per tile) 8 waves of
+      // 32 x 64 on a ring of 4 stages of BK 16
       PGEMM_F32_K2(128, 128, 32, 2, 2, 3, true, vec),
       PGEMM_F32_K2(128, 128, 32, 2, 2, 3, false, ua),
       PGEMM_F32(128, 128, 32, 4, 2, 3, true, vec),
       PGEMM_F32(128, 128, 32, 4, 2, 3, false, ua),
-      PGEMM_F32(128, 128, 16, 4, 2, 4, true, vec),     // ring of 4, BK 16
+      PGEMM_F32(128, 128, 16, 4, 2, 4, true, vec),
       PGEMM_F32(128, 128, 16, 4, 2, 4, false, ua),
       // ring, 4 waves (1 per SIMD)
       PGEMM_F32(256, 256, 16, 2, 2, 3, true, vec),     // wave tile 128 x 128
