@@ -9,7 +9,8 @@
 //    BM x BK of A and BK x BN of B per workgroup.
 //  * 128-bit vector loads (the SGEMM study's float4 step; the "V3.
 //    Vectorized and double buffer" page, measure (1)) become 16-byte global
-//    loads and 16-byte LDS reads and writes.
+//    loads (buffer loads with scalar descriptors and 32-bit lane offsets for
+//    whole tiles) and 16-byte LDS reads and writes.
 //  * Register micro-tiles and warp tiles (SGEMM study, kernels 5, 7 and 9)
 //    become one wave-level tile of RB x CB matrix-core blocks whose
 //    accumulators stay in registers for the whole K loop.
@@ -24,8 +25,11 @@
 //    chunks chosen so that the row-strided operand reads and the stores both
 //    touch distinct banks.
 //  * Edge tiles ("HPC - Lecture 13", kernel 2's note that a general version
-//    must handle inactive threads): out-of-range rows, columns and K entries
-//    load as zero and never touch memory; stores are predicated.
+//    must handle inactive threads): in the steady state, out-of-range rows
+//    and columns are read from the tile's own first row or column (their
+//    products only reach entries that are never stored); in the masked
+//    loads, out-of-range rows, columns and K entries load as zero without
+//    touching memory; stores are predicated.
 //
 // Operand permutations that let one 16-byte LDS read feed several MFMAs
 // without changing the result:
