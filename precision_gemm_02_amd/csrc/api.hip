@@ -79,7 +79,7 @@ struct Tables {
   const Variant<float>* f32;
   const Variant<double>* f64;
   int n32, n64;
-  TileClass f32c[3];
+  TileClass f32c[4];
   TileClass f64c[1];
   Tables() {
     f32 = f32_variants(&n32);
@@ -94,6 +94,15 @@ struct Tables {
     // (2048^3 144.5 against 143.2 TFLOP/s for two K groups of 4 waves).
     f32c[2] = {find_variant(f32, n32, "f32_128x128x16_w4x2_s4_vec"),
                find_variant(f32, n32, "f32_128x128x16_w4x2_s4_ua"), 0.975};
+    // 64 x 64: small problems, and mid-sized ones whose 128 x 128 tiles
+    // would leave a badly filled last round (2500^3 to 3500^3, the ragged
+    // 4097 x 3001 x 1023).  Several of these workgroups share a compute unit
+    // (32 KiB of LDS, ~50 VGPRs); fitted to the measured times of 1280^3 to
+    // 4096^3 under the round model, the class runs at ~0.88 of peak.  1024^3
+    // as one round of 256 tiles: 18.9 us (113.8 TFLOP/s) against 32.8 us for
+    // 128 x 128 tiles split over K.
+    f32c[3] = {find_variant(f32, n32, "f32_64x64x16_w2x2_s4_vec"),
+               find_variant(f32, n32, "f32_64x64x16_w2x2_s4_ua"), 0.88};
     // fp64: 128 x 128 tiles at every size.  Their 64 x 32 wave tiles leave
     // registers for the unrolled steady-state loop, which more than pays for
     // the extra operand traffic of smaller tiles (4096^3: 74.0 TFLOP/s
@@ -195,7 +204,7 @@ int choose(int m, int n, int k, bool vec, bool split_ok) {
   if constexpr (sizeof(T) == 4) {
     table = t.f32;
     cls = t.f32c;
-    ncls = 3;
+    ncls = 4;
   } else {
     table = t.f64;
     cls = t.f64c;
@@ -245,12 +254,14 @@ hipError_t launch_scale(int m, int n, T beta, T* C, int ldc, hipStream_t s) {
                          args, 0, s);
 }
 
+// Launch variant v; with split (decided by pick) the last round's tiles are
+// split over K into ws, whose size pick has checked.
 template <typename T>
 int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, const T* B,
-        int ldb, T beta, T* C, int ldc, T* ws, size_t ws_bytes, hipStream_t s) {
+        int ldb, T beta, T* C, int ldc, bool split, T* ws, size_t ws_bytes, hipStream_t s) {
   if (ceil_div(m, v.bm) * ceil_div(n, v.bn) > kMaxTiles) return PGEMM_EHIP;
   GemmArgs<T> g{};
-  if (ws != nullptr) {
+  if (split && ws != nullptr) {
     const SplitPlan p = split_plan(v, m, n, k, device_cus());
     if (p.split > 1 && ws_bytes >= p.bytes) {
       g.full_tiles = p.full_tiles;
@@ -295,15 +306,18 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
     table = tables().f64;
     count = tables().n64;
   }
-  int idx;
+  int idx, split = 1;
   if (forced >= 0) {
     if (forced >= count) return PGEMM_EVARIANT;
     idx = forced;
     if (table[idx].vec && !vec) return PGEMM_EVARIANT;
   } else {
-    idx = pick<T>(m, n, k, vec, ws != nullptr ? ws_bytes : 0, nullptr);
+    // the split only where pick chose it: a workspace too small for the
+    // preferred split gives exactly the plain entry point's launch, even if
+    // the fallback tiling's own split would fit
+    idx = pick<T>(m, n, k, vec, ws != nullptr ? ws_bytes : 0, &split);
   }
-  return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+  return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, split > 1,
              static_cast<T*>(ws), ws_bytes, s);
 }
 

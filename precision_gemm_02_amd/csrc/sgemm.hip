@@ -42,6 +42,11 @@ const Variant<float>* f32_variants(int* count) {
       // plain double buffering (two LDS stages), 4 waves
       PGEMM_F32(128, 128, 32, 2, 2, 2, true, vec),
       PGEMM_F32(128, 128, 32, 2, 2, 2, false, ua),
+      // 64 x 64 tiles, 4 waves of 32 x 32 on a ring of 4 stages of BK 16:
+      // 256 tiles from 1024^2, and 32 KiB of LDS and ~50 VGPRs, so several
+      // workgroups share a compute unit when there are more tiles than units
+      PGEMM_F32(64, 64, 16, 2, 2, 4, true, vec),
+      PGEMM_F32(64, 64, 16, 2, 2, 4, false, ua),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -125,6 +125,9 @@ def test_selection_by_shape_and_alignment():
     assert name_of(v).startswith("f32_256x256") and name_of(v).endswith("_vec")
     v = pg.select_f32(2048, 2048, 2048, 1.0, FAKE, 2048, FAKE, 2048, 0.0, FAKE, 2048)
     assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_vec")
+    # 1024^2: 256 tiles of 64 x 64
+    v = pg.select_f32(1024, 1024, 1024, 1.0, FAKE, 1024, FAKE, 1024, 0.0, FAKE, 1024)
+    assert name_of(v).startswith("f32_64x64") and name_of(v).endswith("_vec")
     # odd leading dimensions select the unaligned path
     v = pg.select_f32(4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
     assert name_of(v).endswith("_ua")
@@ -195,9 +198,11 @@ def test_workspace_sizes():
     assert pg.workspace_f32(4097, 3001, 1023) == 24 * 10 * 128 * 128 * 4
     # too few K tiles to split after a full round (4 per slice)
     assert pg.workspace_f32(4097, 3001, 100) == 0
-    # fewer tiles than compute units: 1024^3 is 64 tiles of 128^2, each split
-    # into 4 slices (256 / 64) of 8 K tiles
-    assert pg.workspace_f32(1024, 1024, 1024) == 64 * 4 * 128 * 128 * 4
+    # fewer tiles than half the compute units: 512^3 is 64 tiles of 64^2,
+    # each split into 4 slices (256 / 64) of 8 K tiles of 16
+    assert pg.workspace_f32(512, 512, 512) == 64 * 4 * 64 * 64 * 4
+    # 1024^3 is one round of 256 such tiles: no split
+    assert pg.workspace_f32(1024, 1024, 1024) == 0
     # every tiling leaves its last round more than half full: no split
     assert pg.workspace_f32(3840, 3840, 3840) == 0
 
