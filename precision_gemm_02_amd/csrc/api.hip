@@ -80,7 +80,7 @@ struct Tables {
   const Variant<double>* f64;
   int n32, n64;
   TileClass f32c[4];
-  TileClass f64c[1];
+  TileClass f64c[2];
   Tables() {
     f32 = f32_variants(&n32);
     f64 = f64_variants(&n64);
@@ -103,12 +103,17 @@ struct Tables {
     // 128 x 128 tiles split over K.
     f32c[3] = {find_variant(f32, n32, "f32_64x64x16_w2x2_s4_vec"),
                find_variant(f32, n32, "f32_64x64x16_w2x2_s4_ua"), 0.88};
-    // fp64: 128 x 128 tiles at every size.  Their 64 x 32 wave tiles leave
-    // registers for the unrolled steady-state loop, which more than pays for
-    // the extra operand traffic of smaller tiles (4096^3: 74.0 TFLOP/s
-    // against 72.3 for 256 x 128 tiles, whose loop cannot be unrolled).
+    // fp64: 128 x 128 tiles for large problems.  Their 64 x 32 wave tiles
+    // leave registers for the unrolled steady-state loop, which more than
+    // pays for the extra operand traffic of smaller tiles (4096^3: 74.0
+    // TFLOP/s against 72.3 for 256 x 128 tiles, whose loop cannot be
+    // unrolled).  64 x 64 tiles (8 waves of 32 x 16) elsewhere: 1024^3 60.0
+    // against 17.5 TFLOP/s, 3000^3 70.5 against 53.0; fitted under the
+    // round model at ~0.90 of peak.
     f64c[0] = {find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec"),
                find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua"), 0.978};
+    f64c[1] = {find_variant(f64, n64, "f64_64x64x16_w2x4_s3_vec"),
+               find_variant(f64, n64, "f64_64x64x16_w2x4_s3_ua"), 0.90};
   }
 };
 
@@ -175,7 +180,8 @@ SplitPlan split_plan(const Variant<T>& v, int m, int n, int k, int cus) {
 template <typename T>
 double estimate(const Variant<T>& v, double eff, int m, int n, int k, int cus,
                 bool split_ok) {
-  const double unit_s = 2.0 / (157.3e12 / 256);      // one multiply-add per CU
+  // one multiply-add on one compute unit at the precision's matrix peak
+  const double unit_s = 2.0 / ((sizeof(T) == 4 ? 157.3e12 : 78.6e12) / 256);
   const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
   const double c_bytes = (double)cus * v.bm * v.bn * sizeof(T);
@@ -208,7 +214,7 @@ int choose(int m, int n, int k, bool vec, bool split_ok) {
   } else {
     table = t.f64;
     cls = t.f64c;
-    ncls = 1;
+    ncls = 2;
   }
   const int cus = device_cus();
   int best = 0;

@@ -16,7 +16,7 @@ namespace pgemm {
 const Variant<double>* f64_variants(int* count) {
   static const Variant<double> table[] = {
       // LDS ring of 3, 8 waves, wave tile 64 x 32, unrolled steady state:
-      // the default at every size
+      // the large-problem class
       PGEMM_F64(128, 128, 16, 2, 4, 3, true, vec),
       PGEMM_F64(128, 128, 16, 2, 4, 3, false, ua),
       // LDS ring of 3, 8 waves, wave tile 64 x 64 (too many registers to
@@ -27,6 +27,10 @@ const Variant<double>* f64_variants(int* count) {
       PGEMM_F64(256, 128, 16, 2, 4, 2, true, vec),
       PGEMM_F64(128, 128, 16, 2, 2, 2, true, vec),
       PGEMM_F64(128, 128, 16, 2, 2, 2, false, ua),
+      // 64 x 64 tiles, 8 waves of 32 x 16 on a ring of 3: shapes whose
+      // 128 x 128 tiles leave a badly filled last round, and small ones
+      PGEMM_F64(64, 64, 16, 2, 4, 3, true, vec),
+      PGEMM_F64(64, 64, 16, 2, 4, 3, false, ua),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
