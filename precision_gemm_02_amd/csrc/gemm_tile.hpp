@@ -104,7 +104,7 @@ struct GemmArgs {
   // Split of the last, partly filled round of tiles (see split_plan): the
   // first `full_tiles` tiles (in raster order) get one workgroup each; each
   // remaining tile gets `split` workgroups that take consecutive slices of
-  // its K tiles and write raw partial sums to `ws` (split == 0: no split).
+  // its K tiles and write raw partial sums to `ws` (split <= 1: no split).
   int full_tiles;
   int split;
   T* ws;
@@ -135,11 +135,6 @@ __host__ __device__ inline void raster(int t, int tiles_m, int tiles_n, int grou
   const int within = t - group * per_group;
   tm = first_m + within % gsize;
   tn = within / gsize;
-}
-
-__host__ __device__ inline void map_tile(int wg, int tiles_m, int tiles_n, int group_m,
-                                         int& tm, int& tn) {
-  raster(xcd_remap(wg, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 // XOR swizzle of the 16-byte chunks of one Bs row (KC chunks per row), for
@@ -345,13 +340,13 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   // Tiles on the M or N edge take the same loads.  An A chunk whose rows
   // all lie at or beyond M, or a B column at or beyond N, only feeds entries
   // of C that are never stored, so it is read from the tile's first row /
-  // column instead (in bounds; the values do not matter).  An A chunk that straddles M (M
-  // not a multiple of V) is read whole: its elements past row M-1 are the
-  // column's padding or, with a tight lda, the first V-2 rows of the next
-  // column, and again only feed rows that are never stored.  Such reads stay
-  // inside the (K-1)*lda + M elements of A when the column is not the last
-  // one and lda >= V-1, so on the M edge the steady state stops before the
-  // last column (k_whole) and the masked loads take the rest.
+  // column instead (in bounds; the values do not matter).  An A chunk that
+  // straddles M (M not a multiple of V) is read whole: its elements past row
+  // M-1 are the column's padding or, with a tight lda, the first V-2 rows of
+  // the next column, and again only feed rows that are never stored.  Such
+  // reads stay inside the (K-1)*lda + M elements of A when the column is not
+  // the last one and lda >= V-1, so on the M edge the steady state stops
+  // before the last column (k_whole) and the masked loads take the rest.
   static_assert(NT % (BM / V) == 0 && NT % KC == 0, "uniform steps between a thread's chunks");
   // Byte offsets from the tile's first row (A, in the tile's K tile) and
   // first column (B): A chunk i of tile kt is at a_off + i*a_step from
