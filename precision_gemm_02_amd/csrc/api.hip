@@ -169,14 +169,15 @@ SplitPlan split_plan(const Variant<T>& v, int m, int n, int k, int cus) {
 }
 
 // Estimated time of variant v on an m x n x k problem, in multiply-adds of
-// one compute unit at full rate.  Each round of tiles (every compute unit
-// busy with one tile) costs the tile's K loop at the class's efficiency plus
-// a fixed part: ~1.5 us of prologue and the round's stores of C at ~5 TB/s.
-// The last, partly filled round costs a whole round, or with the split of
-// the last round a slice of one plus the fix-up kernel (its HBM traffic at
-// ~4 TB/s and a launch of ~4 us).  Edge tiles cost as much as inner ones
-// (they run the same loop).  On 14 shapes from 1500^3 to 12000 x 2000 x 4000
-// this picks the fastest tile class.
+// one compute unit at the precision's full matrix rate.  Each round of tiles
+// (every compute unit busy with one tile) costs the tile's K loop at the
+// class's efficiency plus a fixed part: ~1.5 us of prologue and the round's
+// stores of C at ~5 TB/s.  The last, partly filled round costs a whole
+// round, or with the split of the last round a slice of one plus the fix-up
+// kernel (its HBM traffic at ~4 TB/s and a launch of ~4 us).  Edge tiles
+// cost as much as inner ones (they run the same loop).  On 20 fp32 shapes
+// from 512^3 to 12000 x 2000 x 4000 and 9 fp64 sizes this picks the
+// fastest tile class (within 1 %).
 template <typename T>
 double estimate(const Variant<T>& v, double eff, int m, int n, int k, int cus,
                 bool split_ok) {
