@@ -4,10 +4,10 @@ One step = one call C <- alpha*A*B + beta*C through the C ABI on inputs that
 are already resident in HBM: gemm_f32 / gemm_f64, or gemm_*_ws with the
 workspace the library asks for when the tiles of C leave a partly filled last
 round (the 4097x3001x1023 workload), or matmat_f64 for the row-major fp64
-workload.  W untimed warmup steps, then K timed steps
-bracketed by torch.cuda.synchronize(); each timed launch is also bracketed by
-HIP events on the stream it is launched on, which gives the kernel's own
-average duration for the roofline figure.
+workload.  W untimed warmup steps, then K timed steps back to back,
+bracketed by torch.cuda.synchronize(); then, outside the timed region, K more
+launches each bracketed by HIP events on the stream they are launched on,
+which give the kernel's own average duration for the roofline figure.
 
 Prints ONE JSON line.  ``value`` is the whole-job throughput in TFLOPS
 (2*M*N*K per step / wall time per step).  ``roofline`` compares the GEMM
@@ -135,8 +135,11 @@ def time_workload(r: Resident, steps: int, warmup: int, min_warm_s: float):
     """W warmup launches, continued until at least ``min_warm_s`` of wall time
     has passed (the GPU raises its clock over a few hundred ms of sustained
     load; a short kernel timed right after an idle gap measures the ramp, not
-    the kernel).  Returns (wall ms per step, kernel ms mean, kernel ms median,
-    warmup launches actually run)."""
+    the kernel).  Then the timed region: exactly ``steps`` launches back to
+    back between two synchronizations (wall clock, nothing else on the
+    stream).  Then, outside it, the same number of launches each between two
+    HIP events on the launch stream, for the kernel's own time.  Returns
+    (wall ms per step, kernel ms mean, kernel ms median, warmup launches)."""
     import torch
     n_warm = 0
     t_end = time.perf_counter() + min_warm_s
@@ -149,17 +152,22 @@ def time_workload(r: Resident, steps: int, warmup: int, min_warm_s: float):
             r.reset_c()   # beta != 0: keep C finite (|beta| > 1 grows it each call)
     r.reset_c()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.launch()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    r.reset_c()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s, e in ev:
         s.record(r.stream)
         r.launch()
         e.record(r.stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     kern_ms = [s.elapsed_time(e) for s, e in ev]
+    r.reset_c()
     return wall / steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms)), n_warm
 
 
