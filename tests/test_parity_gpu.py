@@ -379,21 +379,23 @@ def run_ws(p, ws_bytes=None):
 
 
 # (dtype, m, n, k): each leaves a partly filled last round of tiles on 256
-# compute units and so takes the split path; they cover the tile classes of
-# each precision, ragged M/N edges inside the split tiles and a K tail in
-# the last slice.
+# compute units and so takes the split path (tiling and slices as the library
+# chooses them on 256 units); together they cover every tile class of each
+# precision, ragged M/N edges inside the split tiles and a K tail in the
+# last slice.
 SPLIT_SHAPES = [
-    (np.float32, 2053, 2048, 1000),    # 128^2 tiles: 272 = 256 + 16, 8 slices
-    (np.float32, 2100, 2000, 555),     # 4 slices, K tail of 11
+    (np.float32, 2053, 2048, 1000),    # 128^2 tiles: 272 = 256 + 16, 15 slices
+    (np.float32, 2100, 2000, 555),     # 128^2 tiles, 8 slices, K tail of 11
     (np.float32, 4352, 4096, 640),     # 128^2 tiles: 1088 = 4*256 + 64, 4 slices
-    (np.float32, 8192, 4352, 640),     # 256^2 tiles: 544 = 2*256 + 32, 8 slices
-    (np.float64, 4200, 2048, 300),     # 128^2 fp64 tiles: 528 = 2*256 + 16
-    (np.float64, 2100, 2000, 333),     # 128^2 fp64 tiles, K tail
-    # fewer tiles than compute units: every tile split (at least 2 K tiles each)
-    (np.float32, 512, 512, 512),       # 16 tiles x 8 slices
-    (np.float32, 300, 200, 1000),      # 6 edge tiles x 16 slices of 2 K tiles
-    (np.float64, 200, 130, 333),       # 4 edge tiles x 10 slices, K tail
-    (np.float32, 128, 128, 128),       # one tile, 2 slices
+    (np.float32, 8192, 4352, 640),     # 256x128 tiles: 1088 = 4*256 + 64, 4 slices
+    (np.float64, 4200, 2048, 300),     # 128^2 fp64 tiles: 528 = 2*256 + 16, 4 slices
+    (np.float64, 2100, 2000, 333),     # 64^2 fp64 tiles: 1056 = 4*256 + 32, K tail
+    # fewer tiles than half the compute units: every tile split (at least 2
+    # K tiles each)
+    (np.float32, 512, 512, 512),       # 64 tiles of 64^2 x 4 slices
+    (np.float32, 300, 200, 1000),      # 20 edge tiles x 12 slices
+    (np.float64, 200, 130, 333),       # 12 fp64 edge tiles x 10 slices, K tail
+    (np.float32, 128, 128, 128),       # 4 tiles x 4 slices of 2 K tiles
 ]
 
 
@@ -408,6 +410,51 @@ def test_split_exact_integer(case):
     say("split", np.dtype(dtype).name, (m, n, k), (alpha, beta), "ld", lds, "ws", ws_size(p))
     C = run_ws(p)
     assert_bitwise(C, oracle_full(p))
+
+
+def _random_cases(count, seed, mn_range=(1, 900), k_range=(1, 700)):
+    """Seeded random problems: shapes, leading-dimension padding (odd or
+    chunk-aligned), alpha/beta (zero included) and precision."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for t in range(count):
+        dtype = np.float32 if t % 3 else np.float64
+        m, n = (int(x) for x in rng.integers(mn_range[0], mn_range[1], 2))
+        k = int(rng.integers(k_range[0], k_range[1]))
+        chunk = 4 if dtype == np.float32 else 2
+        if rng.random() < 0.5:          # aligned: every ld a multiple of the chunk
+            up = lambda x: -(-x // chunk) * chunk  # noqa: E731
+            lds = (up(m) + chunk * int(rng.integers(0, 3)), up(k) + chunk * int(rng.integers(0, 3)),
+                   up(m) + chunk * int(rng.integers(0, 3)))
+        else:
+            lds = (m + int(rng.integers(0, 5)), k + int(rng.integers(0, 5)), m + int(rng.integers(0, 5)))
+        alpha, beta = ALPHA_BETA[int(rng.integers(0, len(ALPHA_BETA)))]
+        if rng.random() < 0.1:
+            alpha = 0.0
+        cases.append((dtype, m, n, k, lds, alpha, beta))
+    return cases
+
+
+# small shapes (the 64 x 64 classes, most with the split of every tile) and
+# mid-sized ones (every tile class, splits of a last round)
+RANDOM_CASES = (_random_cases(48, seed=2024)
+                + _random_cases(16, seed=2025, mn_range=(900, 2600), k_range=(1, 1200)))
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_CASES)))
+def test_random_shapes_every_entry_exact_integer(case):
+    """The default entry point (whatever tile class its model picks) and the
+    workspace entry point (with the split it asks for) on seeded random small
+    shapes, aligned or odd leading dimensions: bitwise equal to the oracle on
+    exact-integer inputs, padding and guard bands untouched."""
+    dtype, m, n, k, lds, alpha, beta = RANDOM_CASES[case]
+    p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=600 + case)
+    say("random", np.dtype(dtype).name, (m, n, k), (alpha, beta), "ld", lds, "ws", ws_size(p))
+    R = oracle_full(p)
+    C, _ = run_colmajor(p)
+    assert_bitwise(C, R)
+    if ws_size(p) > 0:
+        assert_bitwise(run_ws(p), R)
 
 
 def test_split_ragged_workload_parity():
