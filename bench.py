@@ -139,7 +139,7 @@ def time_workload(r: Resident, steps: int, warmup: int, min_warm_s: float):
     back between two synchronizations (wall clock, nothing else on the
     stream).  Then, outside it, the same number of launches each between two
     HIP events on the launch stream, for the kernel's own time.  Returns
-    (wall ms per step, kernel ms mean, kernel ms median, warmup launches)."""
+    (wall ms per step, per-launch kernel ms, warmup launches)."""
     import torch
     n_warm = 0
     t_end = time.perf_counter() + min_warm_s
@@ -168,7 +168,7 @@ def time_workload(r: Resident, steps: int, warmup: int, min_warm_s: float):
     torch.cuda.synchronize()
     kern_ms = [s.elapsed_time(e) for s, e in ev]
     r.reset_c()
-    return wall / steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms)), n_warm
+    return wall / steps * 1e3, kern_ms, n_warm
 
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -223,7 +223,11 @@ def recorded_counters(variant: str, workload: str):
             "source": "rocprofv3 --pmc, profiles/ (same built library)"}
 
 
-def roofline(r: Resident, kern_ms_mean: float):
+def roofline(r: Resident, kern_ms: list):
+    """Matrix-core roofline of the GEMM kernel: achieved flops per launch over
+    the mean of the per-launch event times (the median and the minimum are
+    reported beside it)."""
+    kern_ms_mean = float(np.mean(kern_ms))
     achieved = r.flops / (kern_ms_mean * 1e-3) / 1e12
     peak = PEAK_TFLOPS[r.dt]
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
@@ -232,6 +236,8 @@ def roofline(r: Resident, kern_ms_mean: float):
             "counters": recorded_counters(r.variant, r.name),
             "algorithmic_bytes": r.algorithmic_bytes(),
             "kernel": r.variant, "k_split": r.split, "kernel_ms_mean": round(kern_ms_mean, 4),
+            "kernel_ms_median": round(float(np.median(kern_ms)), 4),
+            "kernel_ms_min": round(float(np.min(kern_ms)), 4),
             "entry": r.entry, "workspace_bytes": r.ws_bytes,
             "library_digest": library_digest()}
 
@@ -291,7 +297,7 @@ def sweep(args):
             out = r.C.cpu().numpy()
             got = gi.logical_colmajor(out, p.m, p.n, p.ldc).astype(np.float64)
         r.reset_c()
-        _, _, kern_med, _ = time_workload(r, max(args.steps, 10), args.warmup,
+        _, kern_ms, _ = time_workload(r, max(args.steps, 10), args.warmup,
                                           args.min_warmup_seconds)
         cols = p.n if p.m * p.n * p.k <= 4096 ** 3 else 512
         t0 = time.perf_counter()
@@ -309,6 +315,7 @@ def sweep(args):
         else:
             ok = rel <= 1e-12
         cnt = recorded_counters(r.variant, r.name)
+        kern_med = float(np.median(kern_ms))
         tflops = r.flops / (kern_med * 1e-3) / 1e12
         rows.append((name, "%dx%dx%d" % (p.m, p.n, p.k), r.entry, r.variant, kern_med, tflops,
                      100 * tflops / PEAK_TFLOPS[r.dt], cnt, maxabs, rel, ok, t_or, cols, p.n,
@@ -356,10 +363,11 @@ def main():
         p = r.p
         first_out = r.C[: p.ldc * p.n].view(p.n, p.ldc)[:, : p.m].t().cpu().numpy()
     r.reset_c()
-    ms_step, kern_mean, kern_med, n_warm = time_workload(r, args.steps, args.warmup,
-                                                         args.min_warmup_seconds)
+    ms_step, kern_ms, n_warm = time_workload(r, args.steps, args.warmup,
+                                             args.min_warmup_seconds)
     value = r.flops / (ms_step * 1e-3) / 1e12
-    log("%s: %.3f ms/step, kernel mean %.3f ms -> %.2f TFLOPS" % (r.name, ms_step, kern_mean,
+    log("%s: %.3f ms/step, kernel mean %.3f ms -> %.2f TFLOPS" % (r.name, ms_step,
+                                                                   float(np.mean(kern_ms)),
                                                                    value))
     p = r.p
     out = {
@@ -373,7 +381,7 @@ def main():
                    "layout": "row-major (operand swap)" if p.rowmajor else "column-major",
                    "variant": r.variant, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / PEAK_TFLOPS[r.dt], 2),
-        "roofline": roofline(r, kern_mean),
+        "roofline": roofline(r, kern_ms),
     }
     main_problem = r.p
     secondary = []
@@ -384,9 +392,10 @@ def main():
         torch.cuda.empty_cache()
         r2 = Resident(name)
         steps2 = max(args.steps, 20)
-        ms2, km2, _, nw2 = time_workload(r2, steps2, args.warmup, args.min_warmup_seconds)
+        ms2, km2, nw2 = time_workload(r2, steps2, args.warmup, args.min_warmup_seconds)
         v2 = r2.flops / (ms2 * 1e-3) / 1e12
-        log("%s: %.3f ms/step, kernel mean %.3f ms -> %.2f TFLOPS" % (name, ms2, km2, v2))
+        log("%s: %.3f ms/step, kernel mean %.3f ms -> %.2f TFLOPS" % (name, ms2,
+                                                                       float(np.mean(km2)), v2))
         secondary.append({"workload": name, "value": round(v2, 3), "unit": "TFLOPS",
                           "ms_per_step": round(ms2, 4), "steps": steps2,
                           "warmup_launches": nw2, "dtype": r2.dt,
