@@ -66,7 +66,11 @@ extern "C" {
  * Any leading dimension and any 4-byte-aligned pointer is accepted.  Global
  * memory is moved in 16-byte accesses either way (gfx950 needs only dword
  * alignment for them); 16-byte aligned pointers with leading dimensions that
- * are multiples of 4 select kernels that also assume that alignment.
+ * are multiples of 4 select kernels that also assume that alignment.  The
+ * tile size is chosen per call from the shape.  Leading dimensions so large
+ * that one tile's columns span 2 GiB (about ldb >= 2^21 or lda >= 2^24
+ * elements) take a slower loading path with 64-bit addresses; the results
+ * are the same.
  */
 int gemm_f32(int m, int n, int k, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc,
@@ -100,11 +104,13 @@ int matmat_f64(int lda, int ldb, int ldc, const double *A, const double *B,
 /*
  * Same as gemm_f32 / gemm_f64, with a caller-provided device workspace that
  * lets the library balance the last, partly filled round of tiles: when the
- * tiles of C do not divide evenly over the GPU's compute units, each
- * leftover tile is split into slices of its inner dimension computed by
- * otherwise idle compute units; their partial sums go to the workspace and a
- * second kernel adds them, always in the same slice order, and applies
- * alpha and beta.  Results stay deterministic (identical inputs give
+ * tiles of C leave the last round less than half full (or, for small
+ * problems, most compute units without a tile), each tile of that round is
+ * split into slices of its inner dimension computed by otherwise idle
+ * compute units; their partial sums go to the workspace and a second kernel
+ * adds them, always in the same slice order, and applies alpha and beta.
+ * The tile size may differ from gemm_f32's for the same shape (the one that
+ * is fastest with the split).  Results stay deterministic (identical inputs give
  * identical bits) but are not bitwise equal to gemm_f32's, whose summation
  * order differs.
  *
