@@ -300,6 +300,58 @@ def test_determinism_bitwise():
     assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
 
 
+def test_concurrent_calls_on_two_streams():
+    """Two host threads, each with its own stream (and workspace), launch
+    GEMMs concurrently: fp32 through gemm_f32_ws and fp64 through gemm_f64,
+    eight times each on a fresh copy of C.  Every result is bitwise the one
+    the same call gives alone: the library keeps no per-call state and its
+    launches are ordered only by their own stream."""
+    import threading
+    p32 = exact_problem(np.float32, 2053, 2048, 1000, 1.5, 0.5, (2055, 1001, 2057), seed=700)
+    p64 = exact_problem(np.float64, 900, 1100, 500, 0.75, -1.25, (901, 500, 902), seed=701)
+    ref32 = oracle_full(p32)
+    ref64 = oracle_full(p64)
+    need = ws_size(p32)
+    assert need > 0, "the fp32 case should take the split path"
+    jobs = []
+    for p in (p32, p64):
+        A = torch.from_numpy(p.A).cuda()
+        B = torch.from_numpy(p.B).cuda()
+        C0 = torch.from_numpy(p.C).cuda()
+        jobs.append(dict(p=p, A=A, B=B, C0=C0, C=C0.clone(), s=torch.cuda.Stream()))
+    W = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(j):
+        try:
+            p, s = j["p"], j["s"]
+            with torch.cuda.stream(s):
+                for _ in range(8):
+                    j["C"].copy_(j["C0"])
+                    if p.dtype == np.float32:
+                        pg.gemm_f32_ws(p.m, p.n, p.k, p.alpha, j["A"], p.lda, j["B"], p.ldb,
+                                       p.beta, j["C"], p.ldc, W, need, stream=s)
+                    else:
+                        pg.gemm_f64(p.m, p.n, p.k, p.alpha, j["A"], p.lda, j["B"], p.ldb,
+                                    p.beta, j["C"], p.ldc, stream=s)
+            s.synchronize()
+        except Exception as e:  # noqa: BLE001 (reported below)
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for j, ref in zip(jobs, (ref32, ref64)):
+        p = j["p"]
+        got = logical(j["C"].cpu().numpy(), p.m, p.n, p.ldc)
+        assert_bitwise(got, ref)
+
+
 def test_linearity_bitwise():
     p = gi.make_colmajor_problem("lin", np.float32, 1000, 700, 300, 1000, 300, 1000, 1.0,
                                  0.0, seed=12, c_dist="u")
