@@ -509,6 +509,29 @@ def test_random_shapes_every_entry_exact_integer(case):
         assert_bitwise(run_ws(p), R)
 
 
+LONG_CASES = int(os.environ.get("PGEMM_LONG_TESTS", "0"))
+
+
+@pytest.mark.skipif(LONG_CASES <= 0, reason="set PGEMM_LONG_TESTS=<count> to run")
+def test_random_shapes_long():
+    """Opt-in long run of the random-shape check (PGEMM_LONG_TESTS=3000 takes
+    about a minute): seeded problems up to 3000 x 3000 x 1500, both
+    precisions, odd or aligned leading dimensions, alpha/beta including
+    zero, through gemm_* and gemm_*_ws; bitwise against the oracle."""
+    cases = (_random_cases(LONG_CASES * 7 // 10, seed=77)
+             + _random_cases(LONG_CASES - LONG_CASES * 7 // 10, seed=78,
+                             mn_range=(1, 3000), k_range=(1, 1500)))
+    for t, (dtype, m, n, k, lds, alpha, beta) in enumerate(cases):
+        p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=5000 + t)
+        R = oracle_full(p)
+        C, _ = run_colmajor(p)
+        assert_bitwise(C, R)
+        if ws_size(p) > 0:
+            assert_bitwise(run_ws(p), R)
+        if t % 250 == 0:
+            say("long random", t, np.dtype(dtype).name, (m, n, k), lds, (alpha, beta))
+
+
 def test_split_ragged_workload_parity():
     p = gi.workload("sgemm_ragged")
     assert ws_size(p) > 0
