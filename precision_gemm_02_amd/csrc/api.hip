@@ -107,13 +107,13 @@ struct Tables {
     // leave registers for the unrolled steady-state loop, which more than
     // pays for the extra operand traffic of smaller tiles (4096^3: 74.0
     // TFLOP/s against 72.3 for 256 x 128 tiles, whose loop cannot be
-    // unrolled).  64 x 64 tiles (8 waves of 32 x 16) elsewhere: 1024^3 60.0
-    // against 17.5 TFLOP/s, 3000^3 70.5 against 53.0; fitted under the
-    // round model at ~0.90 of peak.
+    // unrolled).  64 x 64 tiles (8 waves of 32 x 16, a ring of 4) elsewhere:
+    // 1024^3 60.5 against 17.6 TFLOP/s, 3000^3 70.5 against 53.3; fitted
+    // under the round model at ~0.90 of peak.
     f64c[0] = {find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec"),
                find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua"), 0.978};
-    f64c[1] = {find_variant(f64, n64, "f64_64x64x16_w2x4_s3_vec"),
-               find_variant(f64, n64, "f64_64x64x16_w2x4_s3_ua"), 0.90};
+    f64c[1] = {find_variant(f64, n64, "f64_64x64x16_w2x4_s4_vec"),
+               find_variant(f64, n64, "f64_64x64x16_w2x4_s4_ua"), 0.90};
   }
 };
 
