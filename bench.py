@@ -88,9 +88,10 @@ class Resident:
                          p.ldb, p.beta, self.C.data_ptr(), p.ldc)
         self.flops = 2.0 * p.m * p.n * p.k
         self.stream = torch.cuda.current_stream()
-        # A partly filled last round of tiles is split over K slices when the
-        # library is given the workspace it asks for (gemm_*_ws); shapes
-        # that fill whole rounds ask for none and use the plain entry point.
+        # The K iterations of a partly filled last round of tiles are shared
+        # by stream-K workgroups when the library is given the workspace it
+        # asks for (gemm_*_ws); shapes that fill whole rounds ask for none
+        # and use the plain entry point.
         self.ws_bytes = 0
         self.ws = None
         if not p.rowmajor:
@@ -102,10 +103,10 @@ class Resident:
             self.entry = "matmat_f64"
         else:
             self.entry = ("gemm_%s_ws" if self.ws_bytes else "gemm_%s") % self.dt
-        # the kernel the entry point launches, and into how many K slices it
-        # splits the tiles of the last round (1: no split, no fix-up kernel)
+        # the kernel the entry point launches, and how many stream-K
+        # workgroups share the last round (0: none, no fix-up kernel)
         sel = pg.select_ws_f32 if self.dt == "f32" else pg.select_ws_f64
-        vid, self.split = sel(*self.args, self.ws_bytes)
+        vid, self.sk_wgs = sel(*self.args, self.ws_bytes)
         self.variant = pg.variants().get(vid, "none")
 
     def launch(self):
@@ -235,7 +236,7 @@ def roofline(r: Resident, kern_ms: list):
             "traffic": recorded_traffic(r.variant, r.name),
             "counters": recorded_counters(r.variant, r.name),
             "algorithmic_bytes": r.algorithmic_bytes(),
-            "kernel": r.variant, "k_split": r.split, "kernel_ms_mean": round(kern_ms_mean, 4),
+            "kernel": r.variant, "stream_k_wgs": r.sk_wgs, "kernel_ms_mean": round(kern_ms_mean, 4),
             "kernel_ms_median": round(float(np.median(kern_ms)), 4),
             "kernel_ms_min": round(float(np.min(kern_ms)), 4),
             "entry": r.entry, "workspace_bytes": r.ws_bytes,

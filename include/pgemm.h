@@ -103,20 +103,24 @@ int matmat_f64(int lda, int ldb, int ldc, const double *A, const double *B,
 
 /*
  * Same as gemm_f32 / gemm_f64, with a caller-provided device workspace that
- * lets the library balance the last, partly filled round of tiles: when the
- * tiles of C leave the last round less than half full (or, for small
- * problems, most compute units without a tile), each tile of that round is
- * split into slices of its inner dimension computed by otherwise idle
- * compute units; their partial sums go to the workspace and a second kernel
- * adds them, always in the same slice order, and applies alpha and beta.
- * The tile size may differ from gemm_f32's for the same shape (the one that
- * is fastest with the split).  Results stay deterministic (identical inputs give
- * identical bits) but are not bitwise equal to gemm_f32's, whose summation
- * order differs.
+ * lets the library balance the last, partly filled round of tiles by
+ * stream-K: the tiles of the full rounds run one per workgroup as in
+ * gemm_f32, while the K iterations of the remaining tiles are shared evenly
+ * by up to one more workgroup per compute unit.  Each such workgroup writes
+ * the partial sums of its range (the end of one tile and the start of the
+ * next at most) to the workspace, and a second kernel adds each tile's
+ * pieces, always in K order, and applies alpha and beta.  The library uses
+ * it only where its model of the kernel estimates a gain; the tile size may
+ * then differ from gemm_f32's for the same shape.  Results stay
+ * deterministic (identical inputs give identical bits) but are not bitwise
+ * equal to gemm_f32's, whose summation order differs.
  *
  *   workspace        device pointer, 16-byte aligned (argument 12), or NULL
  *   workspace_bytes  its size; pgemm_workspace_f32/f64(m, n, k) returns the
- *                    size this shape can use (0 when no split applies)
+ *                    size this shape can use (0 when stream-K does not
+ *                    apply): two tiles of partial sums per stream-K
+ *                    workgroup, at most 32 MiB (fp32) or 64 MiB (fp64) on
+ *                    256 compute units
  * With NULL or a smaller workspace the call behaves exactly like gemm_f32.
  * The workspace is scratch owned by the caller; calls that share one
  * workspace must be ordered (e.g. on one stream).
@@ -178,17 +182,16 @@ int pgemm_select_f32(int m, int n, int k, float alpha, const float *A, int lda,
 int pgemm_select_f64(int m, int n, int k, double alpha, const double *A, int lda,
                      const double *B, int ldb, double beta, const double *C, int ldc);
 /* The variant gemm_f32_ws / gemm_f64_ws would launch with a workspace of
- * ws_bytes bytes (0: as without one), same return values as above.  If split
- * is not NULL it receives the number of K slices each tile of the last,
- * partly filled round is split into (1: no split; then the call launches
- * only the GEMM kernel, otherwise also the fix-up kernel that sums the
- * slices). */
+ * ws_bytes bytes (0: as without one), same return values as above.  If
+ * sk_wgs is not NULL it receives the number of stream-K workgroups that
+ * share the last, partly filled round (0: none; then the call launches only
+ * the GEMM kernel, otherwise also the fix-up kernel that sums the pieces). */
 int pgemm_select_ws_f32(int m, int n, int k, float alpha, const float *A, int lda,
                         const float *B, int ldb, float beta, const float *C, int ldc,
-                        size_t ws_bytes, int *split);
+                        size_t ws_bytes, int *sk_wgs);
 int pgemm_select_ws_f64(int m, int n, int k, double alpha, const double *A, int lda,
                         const double *B, int ldb, double beta, const double *C, int ldc,
-                        size_t ws_bytes, int *split);
+                        size_t ws_bytes, int *sk_wgs);
 const char *pgemm_variant_name(int variant);
 int pgemm_num_variants(void);
 int gemm_f32_variant(int variant, int m, int n, int k, float alpha, const float *A,

@@ -218,19 +218,19 @@ def select_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
 
 
 def select_ws_f32(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws_bytes):
-    """(variant id, K slices of the split tiles) gemm_f32_ws would use."""
-    split = ctypes.c_int(1)
+    """(variant id, stream-K workgroups) gemm_f32_ws would use (0: none)."""
+    sk = ctypes.c_int(0)
     v = _lib.pgemm_select_ws_f32(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
-                                 _addr(C), ldc, ws_bytes, ctypes.byref(split))
-    return v, split.value
+                                 _addr(C), ldc, ws_bytes, ctypes.byref(sk))
+    return v, sk.value
 
 
 def select_ws_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws_bytes):
-    """(variant id, K slices of the split tiles) gemm_f64_ws would use."""
-    split = ctypes.c_int(1)
+    """(variant id, stream-K workgroups) gemm_f64_ws would use (0: none)."""
+    sk = ctypes.c_int(0)
     v = _lib.pgemm_select_ws_f64(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
-                                 _addr(C), ldc, ws_bytes, ctypes.byref(split))
-    return v, split.value
+                                 _addr(C), ldc, ws_bytes, ctypes.byref(sk))
+    return v, sk.value
 
 
 def variants():

@@ -100,7 +100,7 @@ struct Tables {
     // (32 KiB of LDS, ~50 VGPRs); fitted to the measured times of 1280^3 to
     // 4096^3 under the round model, the class runs at ~0.88 of peak.  1024^3
     // as one round of 256 tiles: 18.9 us (113.8 TFLOP/s) against 32.8 us for
-    // 128 x 128 tiles split over K.
+    // 64 tiles of 128 x 128, each with its K loop split over 4 workgroups.
     f32c[3] = {find_variant(f32, n32, "f32_64x64x16_w2x2_s4_vec"),
                find_variant(f32, n32, "f32_64x64x16_w2x2_s4_ua"), 0.88};
     // fp64: 128 x 128 tiles for large problems.  Their 64 x 32 wave tiles
@@ -138,33 +138,34 @@ int device_cus() {
   return v;
 }
 
-// Split of the last round of tiles.  With T tiles on P compute units, the
-// first R = floor(T/P) rounds stay one tile per workgroup; if the remaining
-// Tr = T - R*P tiles would leave more than half the compute units idle in a
-// last round, each of them is split into s K slices (s*Tr <= P) whose partial
-// sums go to the workspace and are added, in slice order, by the fix-up
-// kernel.  Slices keep at least 4 K tiles after a full round (the split
-// tiles then run beside nothing else) and at least 2 when there is no full
-// round (T < P/2: small problems, where the split is the only parallelism).
-struct SplitPlan {
-  int full_tiles = 0, split = 1;
+// Stream-K for the last round of tiles.  With T tiles on P compute units,
+// the first R = floor(T/P) rounds stay one tile per workgroup; the K tiles of
+// the remaining Tr = T - R*P tiles (I = Tr*nk iterations) are shared evenly
+// by S more workgroups, S <= P and S > Tr so that tiles are shared, each
+// taking at least 4 K tiles after a full round (the shared tiles then run
+// beside nothing else) or 2 without one (small problems).  A workgroup's
+// range covers the end of one tile and the start of the next at most; each
+// piece's partial sums go to the workspace (two slots per workgroup) and the
+// fix-up kernel adds each tile's pieces in K order.
+struct SkPlan {
+  int full_tiles = 0, wgs = 0;
   size_t bytes = 0;
 };
 
 template <typename T>
-SplitPlan split_plan(const Variant<T>& v, int m, int n, int k, int cus) {
-  SplitPlan p;
+SkPlan sk_plan(const Variant<T>& v, int m, int n, int k, int cus) {
+  SkPlan p;
   const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
   const long long nk = ceil_div(k, v.bk);
-  if (rest == 0 || rest * 2 > cus) return p;
-  long long s = cus / rest;
-  const long long min_slice = rounds >= 1 ? 4 : 2;
-  if (s > nk / min_slice) s = nk / min_slice;
-  if (s < 2) return p;
+  if (rest == 0) return p;
+  const long long min_iters = rounds >= 1 ? 4 : 2;
+  long long S = rest * nk / min_iters;
+  if (S > cus) S = cus;
+  if (S <= rest) return p;
   p.full_tiles = (int)(rounds * cus);
-  p.split = (int)s;
-  p.bytes = (size_t)rest * (size_t)s * (size_t)v.bm * (size_t)v.bn * sizeof(T);
+  p.wgs = (int)S;
+  p.bytes = (size_t)2 * (size_t)S * (size_t)v.bm * (size_t)v.bn * sizeof(T);
   return p;
 }
 
@@ -173,37 +174,50 @@ SplitPlan split_plan(const Variant<T>& v, int m, int n, int k, int cus) {
 // (every compute unit busy with one tile) costs the tile's K loop at the
 // class's efficiency plus a fixed part: ~1.5 us of prologue and the round's
 // stores of C at ~5 TB/s.  The last, partly filled round costs a whole
-// round, or with the split of the last round a slice of one plus the fix-up
-// kernel (its HBM traffic at ~4 TB/s and a launch of ~4 us).  Edge tiles
-// cost as much as inner ones (they run the same loop).  On 20 fp32 shapes
-// from 512^3 to 12000 x 2000 x 4000 and 9 fp64 sizes this picks the
+// round, or with stream-K (`sk`) each workgroup's share of its K iterations,
+// the fixed part of one or two pieces and the fix-up kernel (its HBM
+// traffic at ~4 TB/s and ~8 us for its launch behind the GEMM kernel and the
+// uneven end of the pieces, fitted to 29 measured shapes).  Edge tiles cost
+// as much as inner ones (they run the same loop).  On 20 fp32 shapes from
+// 512^3 to 12000 x 2000 x 4000 and 9 fp64 sizes the plain estimate picks the
 // fastest tile class (within 1 %).
 template <typename T>
-double estimate(const Variant<T>& v, double eff, int m, int n, int k, int cus,
-                bool split_ok) {
+double estimate(const Variant<T>& v, double eff, int m, int n, int k, int cus, bool sk) {
   // one multiply-add on one compute unit at the precision's matrix peak
   const double unit_s = 2.0 / ((sizeof(T) == 4 ? 157.3e12 : 78.6e12) / 256);
   const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
   const double c_bytes = (double)cus * v.bm * v.bn * sizeof(T);
-  const double round =
-      (double)v.bm * (double)v.bn * (double)k / eff + (1.5e-6 + c_bytes / 5e12) / unit_s;
-  double t = (double)rounds * round;
+  const double kloop = (double)v.bm * (double)v.bn * (double)k / eff;
+  const double fixed = (1.5e-6 + c_bytes / 5e12) / unit_s;
+  const double t = (double)rounds * (kloop + fixed);
   if (rest == 0) return t;
-  if (split_ok) {
-    const SplitPlan p = split_plan(v, m, n, k, cus);
-    if (p.split > 1) {
-      const double fix_bytes = (double)(p.split + 2) * (double)rest * v.bm * v.bn * sizeof(T);
-      return t + round / p.split + (fix_bytes / 4e12 + 4e-6) / unit_s;
+  if (sk) {
+    const SkPlan p = sk_plan(v, m, n, k, cus);
+    if (p.wgs > 0) {
+      const long long nk = ceil_div(k, v.bk), iters = rest * nk;
+      const long long per_wg = ceil_div(iters, p.wgs);
+      // two pieces (two prologues and epilogues) unless every range lies
+      // inside one tile
+      const bool aligned = iters % p.wgs == 0 && nk % per_wg == 0;
+      const double tile_bytes = (double)v.bm * v.bn * sizeof(T);
+      const double fix_bytes = ((double)p.wgs + 3.0 * (double)rest) * tile_bytes;
+      return t + kloop * (double)per_wg / (double)nk + (aligned ? 1 : 2) * fixed +
+             (fix_bytes / 4e12 + 8e-6) / unit_s;
     }
   }
-  return t + round;
+  return t + kloop + fixed;
 }
 
-// Variant table index for this shape and alignment: the tile class with
-// the least estimated time (with the split of the last round if split_ok).
+// The tile class with the least estimated time for this shape (with
+// stream-K of the last round where sk_ok and where it is estimated to help).
+struct Choice {
+  int cls = 0;
+  bool sk = false;
+};
+
 template <typename T>
-int choose(int m, int n, int k, bool vec, bool split_ok) {
+Choice choose(int m, int n, int k, bool sk_ok) {
   const Tables& t = tables();
   const Variant<T>* table;
   const TileClass* cls;
@@ -218,38 +232,58 @@ int choose(int m, int n, int k, bool vec, bool split_ok) {
     ncls = 2;
   }
   const int cus = device_cus();
-  int best = 0;
+  if (k <= 0) k = 1;
+  Choice best;
   double best_t = 0;
   for (int c = 0; c < ncls; ++c) {
-    const double e =
-        estimate(table[cls[c].vec], cls[c].eff, m, n, k > 0 ? k : 1, cus, split_ok);
+    const Variant<T>& v = table[cls[c].vec];
+    double e = estimate(v, cls[c].eff, m, n, k, cus, false);
+    bool sk = false;
+    if (sk_ok && v.sk && sk_plan(v, m, n, k, cus).wgs > 0) {
+      // stream-K only where it is estimated at least 1 % faster: below that
+      // the measured gains were within noise or losses
+      const double e_sk = estimate(v, cls[c].eff, m, n, k, cus, true);
+      if (e_sk * 1.01 < e) {
+        e = e_sk;
+        sk = true;
+      }
+    }
     if (c == 0 || e < best_t) {
-      best = c;
+      best = {c, sk};
       best_t = e;
     }
   }
-  return vec ? cls[best].vec : cls[best].ua;
+  return best;
 }
 
-// The variant a call launches: with a workspace large enough for its split
-// plan, the tiling that is best with the split of the last round; otherwise
-// the best one without it.  *split (if given) receives the number of K slices
-// of the split tiles, 1 when there is no split.
+// The variant a call launches and its stream-K plan: with a workspace large
+// enough for the plan of the class that is best with stream-K, that class
+// and plan; otherwise the best class without it (and an empty plan).
 template <typename T>
-int pick(int m, int n, int k, bool vec, size_t ws_bytes, int* split) {
+int pick(int m, int n, int k, bool vec, size_t ws_bytes, SkPlan* plan) {
+  const Tables& t = tables();
   const Variant<T>* table;
-  if constexpr (sizeof(T) == 4) table = tables().f32;
-  else table = tables().f64;
-  if (split != nullptr) *split = 1;
+  const TileClass* cls;
+  if constexpr (sizeof(T) == 4) {
+    table = t.f32;
+    cls = t.f32c;
+  } else {
+    table = t.f64;
+    cls = t.f64c;
+  }
+  *plan = SkPlan{};
   if (ws_bytes > 0) {
-    const int w = choose<T>(m, n, k, vec, true);
-    const SplitPlan p = split_plan(table[w], m, n, k, device_cus());
-    if (p.split > 1 && ws_bytes >= p.bytes) {
-      if (split != nullptr) *split = p.split;
-      return w;
+    const Choice c = choose<T>(m, n, k, true);
+    if (c.sk) {
+      const SkPlan p = sk_plan(table[cls[c.cls].vec], m, n, k, device_cus());
+      if (ws_bytes >= p.bytes) {
+        *plan = p;
+        return vec ? cls[c.cls].vec : cls[c.cls].ua;
+      }
     }
   }
-  return choose<T>(m, n, k, vec, false);
+  const Choice c = choose<T>(m, n, k, false);
+  return vec ? cls[c.cls].vec : cls[c.cls].ua;
 }
 
 template <typename T>
@@ -261,20 +295,17 @@ hipError_t launch_scale(int m, int n, T beta, T* C, int ldc, hipStream_t s) {
                          args, 0, s);
 }
 
-// Launch variant v; with split (decided by pick) the last round's tiles are
-// split over K into ws, whose size pick has checked.
+// Launch variant v; with a stream-K plan (decided by pick, whose workspace
+// size pick has checked) the last round's tiles are shared through ws.
 template <typename T>
 int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, const T* B,
-        int ldb, T beta, T* C, int ldc, bool split, T* ws, size_t ws_bytes, hipStream_t s) {
+        int ldb, T beta, T* C, int ldc, const SkPlan& plan, T* ws, hipStream_t s) {
   if (ceil_div(m, v.bm) * ceil_div(n, v.bn) > kMaxTiles) return PGEMM_EHIP;
   GemmArgs<T> g{};
-  if (split && ws != nullptr) {
-    const SplitPlan p = split_plan(v, m, n, k, device_cus());
-    if (p.split > 1 && ws_bytes >= p.bytes) {
-      g.full_tiles = p.full_tiles;
-      g.split = p.split;
-      g.ws = ws;
-    }
+  if (plan.wgs > 0 && ws != nullptr) {
+    g.full_tiles = plan.full_tiles;
+    g.sk_wgs = plan.wgs;
+    g.ws = ws;
   }
   g.M = m;
   g.N = n;
@@ -313,41 +344,47 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
     table = tables().f64;
     count = tables().n64;
   }
-  int idx, split = 1;
+  int idx;
+  SkPlan plan;
   if (forced >= 0) {
     if (forced >= count) return PGEMM_EVARIANT;
     idx = forced;
     if (table[idx].vec && !vec) return PGEMM_EVARIANT;
   } else {
-    // the split only where pick chose it: a workspace too small for the
-    // preferred split gives exactly the plain entry point's launch, even if
-    // the fallback tiling's own split would fit
-    idx = pick<T>(m, n, k, vec, ws != nullptr ? ws_bytes : 0, &split);
+    // stream-K only where pick chose it: a workspace too small for the
+    // preferred plan gives exactly the plain entry point's launch, even if
+    // the fallback tiling's own plan would fit
+    idx = pick<T>(m, n, k, vec, ws != nullptr ? ws_bytes : 0, &plan);
   }
-  return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, split > 1,
-             static_cast<T*>(ws), ws_bytes, s);
+  return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, plan,
+             static_cast<T*>(ws), s);
 }
 
-// Workspace the split path would use for this shape (0: no split).
+// Workspace the stream-K path would use for this shape (0: none).
 template <typename T>
 size_t workspace_impl(int m, int n, int k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
   const Tables& t = tables();
+  const Choice c = choose<T>(m, n, k, true);
+  if (!c.sk) return 0;
   // the aligned and unaligned variants of a tile class share their tiling
-  const int w = choose<T>(m, n, k, true, true);
-  if constexpr (sizeof(T) == 4) return split_plan(t.f32[w], m, n, k, device_cus()).bytes;
-  else return split_plan(t.f64[w], m, n, k, device_cus()).bytes;
+  if constexpr (sizeof(T) == 4)
+    return sk_plan(t.f32[t.f32c[c.cls].vec], m, n, k, device_cus()).bytes;
+  else
+    return sk_plan(t.f64[t.f64c[c.cls].vec], m, n, k, device_cus()).bytes;
 }
 
 template <typename T>
 int select_impl(int m, int n, int k, T alpha, const T* A, int lda, const T* B, int ldb,
-                const T* C, int ldc, size_t ws_bytes, int* split) {
-  if (split != nullptr) *split = 1;
+                const T* C, int ldc, size_t ws_bytes, int* sk_wgs) {
+  if (sk_wgs != nullptr) *sk_wgs = 0;
   const int st = check_args(m, n, k, alpha, A, lda, B, ldb, C, ldc);
   if (st != 0) return st;
   if (m == 0 || n == 0 || k == 0 || alpha == T(0)) return 0;
   const bool vec = vec_ok(A, lda, B, ldb, C, ldc);
-  const int idx = pick<T>(m, n, k, vec, ws_bytes, split);
+  SkPlan plan;
+  const int idx = pick<T>(m, n, k, vec, ws_bytes, &plan);
+  if (sk_wgs != nullptr) *sk_wgs = plan.wgs;
   if constexpr (sizeof(T) == 4) return 1 + idx;
   else return 1 + tables().n32 + idx;
 }
@@ -491,16 +528,16 @@ int pgemm_select_f64(int m, int n, int k, double alpha, const double* A, int lda
 
 int pgemm_select_ws_f32(int m, int n, int k, float alpha, const float* A, int lda,
                         const float* B, int ldb, float beta, const float* C, int ldc,
-                        size_t ws_bytes, int* split) {
+                        size_t ws_bytes, int* sk_wgs) {
   (void)beta;
-  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, split);
+  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, sk_wgs);
 }
 
 int pgemm_select_ws_f64(int m, int n, int k, double alpha, const double* A, int lda,
                         const double* B, int ldb, double beta, const double* C, int ldc,
-                        size_t ws_bytes, int* split) {
+                        size_t ws_bytes, int* sk_wgs) {
   (void)beta;
-  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, split);
+  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, sk_wgs);
 }
 
 int pgemm_num_variants(void) { return tables().n32 + tables().n64; }

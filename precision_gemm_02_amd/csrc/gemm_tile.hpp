@@ -101,12 +101,13 @@ struct GemmArgs {
   int lda, ldb, ldc;
   int tiles_m, tiles_n;
   int group_m;     // tile rows per raster group
-  // Split of the last, partly filled round of tiles (see split_plan): the
-  // first `full_tiles` tiles (in raster order) get one workgroup each; each
-  // remaining tile gets `split` workgroups that take consecutive slices of
-  // its K tiles and write raw partial sums to `ws` (split <= 1: no split).
+  // Stream-K for the last, partly filled round of tiles (see sk_plan): the
+  // first `full_tiles` tiles (in raster order) get one workgroup each; the
+  // K tiles of the remaining ones are shared evenly by `sk_wgs` more
+  // workgroups, which write raw partial sums to `ws` (full_tiles == all
+  // tiles: no stream-K).
   int full_tiles;
-  int split;
+  int sk_wgs;
   T* ws;
   // Nonzero when every offset of a whole-tile load from its tile's first
   // row/column fits a signed 32-bit byte count (see buffer_offsets_fit);
@@ -286,7 +287,10 @@ __host__ inline bool buffer_offsets_fit(int bm, int bn, int bk, long long lda, l
 }
 
 // ---------------------------------------------------------------- kernel
-template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS>
+// SKP: the stream-K form (a workgroup may run two pieces, and pieces may go
+// to the workspace); without it every workgroup is one whole tile into C.
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS,
+          bool SKP>
 __global__ void __launch_bounds__(WGM * WGN * 64 * KS)
 gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>;
@@ -302,19 +306,29 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   // stage, an access is one per-thread base plus an immediate offset).
   __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
 
-  // Tile and range of K tiles of this workgroup.
+  // Pieces of work of this workgroup: a tile, a range [kt_begin, kt_end) of
+  // its K tiles and a destination (C, or a workspace slot for partial sums).
+  // A workgroup of the full rounds has one piece: a whole tile into C.  The
+  // stream-K workgroups (blockIdx >= full_tiles) share the K tiles of the
+  // remaining tiles evenly: workgroup w takes iterations [w*I/P, (w+1)*I/P)
+  // of the I = rest*nk iterations in (tile, K tile) order, which is the end
+  // of one tile and the start of the next at most (P >= rest); piece j of
+  // workgroup w writes its raw partial sums to workspace slot 2w + j.
   const int nk_all = (g.K + BK - 1) / BK;
-  int t_lin, kt_begin = 0, kt_end = nk_all, slice = -1, r = 0;
-  if ((int)blockIdx.x < g.full_tiles) {
-    t_lin = xcd_remap(blockIdx.x, g.full_tiles);
-  } else {
-    const int u = blockIdx.x - g.full_tiles;
-    r = u / g.split;
-    slice = u - r * g.split;
-    t_lin = g.full_tiles + r;
-    kt_begin = (int)((long long)slice * nk_all / g.split);
-    kt_end = (int)((long long)(slice + 1) * nk_all / g.split);
+  const bool sk_wg = SKP && (int)blockIdx.x >= g.full_tiles;
+  const int w_sk = (int)blockIdx.x - g.full_tiles;
+  long long sk_b0 = 0, sk_b1 = 0;
+  int sk_r0 = 0, npieces = 1;
+  if (sk_wg) {
+    const long long rest = (long long)g.tiles_m * g.tiles_n - g.full_tiles;
+    const long long iters = rest * nk_all;
+    sk_b0 = (long long)w_sk * iters / g.sk_wgs;
+    sk_b1 = (long long)(w_sk + 1) * iters / g.sk_wgs;
+    sk_r0 = (int)(sk_b0 / nk_all);
+    npieces = (sk_b1 > (long long)(sk_r0 + 1) * nk_all) ? 2 : 1;
   }
+  auto tile_piece = [&](const int t_lin, const int kt_begin, const int kt_end,
+                        const int slot) __attribute__((always_inline)) {
   int tm, tn;
   raster(t_lin, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -480,8 +494,8 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   constexpr int NG = BK / KG;      // inner-index groups per K tile
   constexpr int NGL = NG / KS;     // groups per K tile for one wave
   const int kg0 = kgrp * NGL * KG; // this wave's first inner index in a tile
-  // This workgroup's K tiles: [kt_begin, kt_end) (all of them unless the
-  // tile's K range is split over several workgroups).
+  // This piece's K tiles: [kt_begin, kt_end) (all of them unless stream-K
+  // workgroups share the tile).
 
   if constexpr (STAGES == 2) {
     // Two LDS stages.  Tile t+1 is fetched from HBM into registers while
@@ -695,11 +709,11 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     if (kgrp == 1) return;
   }
 
-  // Destination: C, or for a K slice of a split tile its raw partial sums
-  // (alpha = 1, beta = 0, all BM x BN elements, column-major with ld = BM)
-  // in workspace slot (remainder tile r, slice).
-  const bool to_ws = slice >= 0;
-  T* const cbase = to_ws ? g.ws + (size_t)(r * g.split + slice) * (BM * BN) : g.C;
+  // Destination: C, or for a stream-K piece its raw partial sums (alpha = 1,
+  // beta = 0, all BM x BN elements, column-major with ld = BM) in workspace
+  // slot `slot`.
+  const bool to_ws = slot >= 0;
+  T* const cbase = to_ws ? g.ws + (size_t)slot * (BM * BN) : g.C;
   const int ldc = to_ws ? BM : g.ldc;
   const T alpha = to_ws ? T(1) : g.alpha, beta = to_ws ? T(0) : g.beta;
   const bool read_c = beta != T(0);
@@ -935,13 +949,42 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       }
     }
   }
+  };  // tile_piece
+
+  if constexpr (!SKP) {
+    tile_piece(xcd_remap(blockIdx.x, g.full_tiles), 0, nk_all, -1);
+  } else {
+    // (the K-group hand-over's early exit would break the barrier between
+    // pieces)
+    static_assert(KS == 1, "stream-K pieces need one K group");
+    for (int pc = 0; pc < npieces; ++pc) {
+      int t_lin, kb = 0, ke = nk_all, slot = -1;
+      if (!sk_wg) {
+        t_lin = xcd_remap(blockIdx.x, g.full_tiles);
+      } else {
+        // the previous piece's epilogue has finished with the LDS
+        if (pc > 0) __syncthreads();
+        const int r = sk_r0 + pc;
+        const long long first = (long long)r * nk_all;
+        t_lin = g.full_tiles + r;
+        if (pc == 0) kb = (int)(sk_b0 - first);
+        if (sk_b1 - first < nk_all) ke = (int)(sk_b1 - first);
+        slot = 2 * w_sk + pc;
+      }
+      // one call site: the body is inlined once
+      tile_piece(t_lin, kb, ke, slot);
+    }
+  }
 }
 
-// Fix-up of split tiles: C = alpha * (sum over the K slices, in slice order)
-// + beta * C for every element of the remainder tiles that lies inside C.
-// One thread per element; block y = remainder tile.
+// Fix-up of the stream-K tiles: C = alpha * (sum of the pieces' partial
+// sums, in K order) + beta * C for every element of the remaining tiles that
+// lies inside C.  Tile r's pieces come from the stream-K workgroups whose
+// iteration ranges meet [r*nk, (r+1)*nk): workgroup w's piece is its slot 2w
+// if its range starts in tile r, 2w + 1 if it started in tile r - 1.  One
+// thread per element; block y = remaining tile.
 template <typename T>
-__global__ void __launch_bounds__(256) split_fixup_kernel(GemmArgs<T> g, int bm, int bn) {
+__global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs<T> g, int bm, int bn, int bk) {
   const int r = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;   // element of the tile, ld = bm
   if (e >= bm * bn) return;
@@ -949,10 +992,21 @@ __global__ void __launch_bounds__(256) split_fixup_kernel(GemmArgs<T> g, int bm,
   raster(g.full_tiles + r, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
   const int i = tm * bm + e % bm, j = tn * bn + e / bm;
   if (i >= g.M || j >= g.N) return;
+  const long long nk = (g.K + bk - 1) / bk;
+  const long long rest = (long long)g.tiles_m * g.tiles_n - g.full_tiles;
+  const long long iters = rest * nk, P = g.sk_wgs;
+  const long long lo = (long long)r * nk, hi = lo + nk;
+  // b(w) = w*iters/P; the first workgroup whose range ends past lo
+  long long w = (lo * P) / iters;
+  while (w > 0 && (w * iters) / P > lo) --w;
+  while (((w + 1) * iters) / P <= lo) ++w;
   const size_t slot = (size_t)bm * bn;
-  const T* p = g.ws + (size_t)r * g.split * slot + e;
-  T sum = p[0];
-  for (int sl = 1; sl < g.split; ++sl) sum += p[sl * slot];
+  T sum = T(0);
+  for (; w < P && (w * iters) / P < hi; ++w) {
+    const long long b = (w * iters) / P;
+    const int piece = (b >= lo) ? 0 : 1;
+    sum += g.ws[(size_t)(2 * w + piece) * slot + e];
+  }
   T* pc = g.C + (size_t)j * g.ldc + i;
   T v = g.alpha * sum;
   if (g.beta != T(0)) v = __builtin_fma(g.beta, *pc, v);

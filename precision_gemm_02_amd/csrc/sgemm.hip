@@ -8,18 +8,25 @@
 
 namespace pgemm {
 
-#define PGEMM_F32(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                 \
-  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, \
+#define PGEMM_F32(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                        \
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, false, \
    &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S>}
+// The same with the stream-K form compiled in (the tile classes the shape
+// choice uses).
+#define PGEMM_F32_SK(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                    \
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, true, \
+   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 1, true>}
 // _k2: two groups of WM x WN waves split each K tile's inner indices.
-#define PGEMM_F32_K2(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                   \
-  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, \
+#define PGEMM_F32_K2(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                          \
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, false, \
    &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2>}
 
 // A host function owns the table so that it is never treated as device data.
 const Variant<float>* f32_variants(int* count) {
   static const Variant<float> table[] = {
-      // LDS ring of 3, 8 waves (2 per SIMD), wave tile 128 x 64: large problems
+      // LDS ring of 3, 8 waves (2 per SIMD), wave tile 128 x 64: large
+      // problems (no stream-K form: with its piece loop the 128 x 64 wave
+      // tile no longer fits the registers)
       PGEMM_F32(256, 256, 16, 2, 4, 3, true, vec),
       PGEMM_F32(256, 256, 16, 2, 4, 3, false, ua),
       // 256 x 128 tiles, 8 waves of 64 x 64: shapes where whole rounds of
@@ -34,8 +41,8 @@ const Variant<float>* f32_variants(int* count) {
       PGEMM_F32_K2(128, 128, 32, 2, 2, 3, false, ua),
       PGEMM_F32(128, 128, 32, 4, 2, 3, true, vec),
       PGEMM_F32(128, 128, 32, 4, 2, 3, false, ua),
-      PGEMM_F32(128, 128, 16, 4, 2, 4, true, vec),
-      PGEMM_F32(128, 128, 16, 4, 2, 4, false, ua),
+      PGEMM_F32_SK(128, 128, 16, 4, 2, 4, true, vec),
+      PGEMM_F32_SK(128, 128, 16, 4, 2, 4, false, ua),
       // ring, 4 waves (1 per SIMD)
       PGEMM_F32(256, 256, 16, 2, 2, 3, true, vec),     // wave tile 128 x 128
       PGEMM_F32(128, 128, 16, 2, 2, 4, true, vec),     // wave tile 64 x 64
@@ -45,8 +52,8 @@ const Variant<float>* f32_variants(int* count) {
       // 64 x 64 tiles, 4 waves of 32 x 32 on a ring of 4 stages of BK 16:
       // 256 tiles from 1024^2, and 32 KiB of LDS and ~50 VGPRs, so several
       // workgroups share a compute unit when there are more tiles than units
-      PGEMM_F32(64, 64, 16, 2, 2, 4, true, vec),
-      PGEMM_F32(64, 64, 16, 2, 2, 4, false, ua),
+      PGEMM_F32_SK(64, 64, 16, 2, 2, 4, true, vec),
+      PGEMM_F32_SK(64, 64, 16, 2, 2, 4, false, ua),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -15,14 +15,17 @@ struct Variant {
   const char* name;
   int bm, bn, bk;
   bool vec;        // needs 16-byte aligned pointers and leading dims
+  bool sk;         // has the stream-K form
   LaunchFn<T> launch;
 };
 
 // Launch one tile configuration.  Plain: one workgroup per BM x BN tile of
-// C.  Split (a.split > 1): one workgroup per tile for the first a.full_tiles
-// tiles and a.split workgroups (K slices writing partial sums to a.ws) for
-// each remaining tile, then the fix-up kernel.
-template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS = 1>
+// C.  Stream-K (SK compiled in, a.sk_wgs > 0 with a workspace): one
+// workgroup per tile for the first a.full_tiles tiles, a.sk_wgs workgroups
+// that share the K tiles of the remaining ones (partial sums to a.ws), then
+// the fix-up kernel.  Without SK a stream-K request runs plain.
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS = 1,
+          bool SK = false>
 hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
   using T = typename TR::T;
   GemmArgs<T> g = a;
@@ -30,21 +33,25 @@ hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
   g.tiles_n = (g.N + BN - 1) / BN;
   const int tiles = g.tiles_m * g.tiles_n;
   if (g.group_m <= 0) g.group_m = 4;
-  if (g.split <= 1 || g.ws == nullptr || g.full_tiles >= tiles) {
+  if (!SK || g.sk_wgs <= 0 || g.ws == nullptr || g.full_tiles >= tiles) {
     g.full_tiles = tiles;
-    g.split = 1;
+    g.sk_wgs = 0;
   }
   const int rest = tiles - g.full_tiles;
   g.buf32 = buffer_offsets_fit<T>(BM, BN, BK, g.lda, g.ldb) ? 1 : 0;
   void* args[] = {&g};
-  const dim3 grid((unsigned)(g.full_tiles + rest * g.split)), block(WGM * WGN * 64 * KS);
-  hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>),
-      grid, block, args, 0, stream);
+  const dim3 grid((unsigned)(g.full_tiles + g.sk_wgs)), block(WGM * WGN * 64 * KS);
+  const void* kern =
+      rest == 0
+          ? reinterpret_cast<const void*>(
+                &gemm_tile_kernel<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS, false>)
+          : reinterpret_cast<const void*>(
+                &gemm_tile_kernel<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS, SK>);
+  hipError_t e = hipLaunchKernel(kern, grid, block, args, 0, stream);
   if (e != hipSuccess || rest == 0) return e;
-  int bm = BM, bn = BN;
-  void* fargs[] = {&g, &bm, &bn};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&split_fixup_kernel<T>),
+  int bm = BM, bn = BN, bk = BK;
+  void* fargs[] = {&g, &bm, &bn, &bk};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&sk_fixup_kernel<T>),
                          dim3((unsigned)((BM * BN + 255) / 256), (unsigned)rest), dim3(256),
                          fargs, 0, stream);
 }

@@ -142,23 +142,28 @@ def test_selection_by_shape_and_alignment():
 
 def test_selection_with_workspace():
     # the ragged 4097 x 3001 x 1023 problem: with the workspace it asks for,
-    # 128 x 128 tiles with the 24 leftover tiles split into 10 K slices;
-    # without it, the plain choice (no split)
+    # 128 x 128 tiles (3 full rounds of 256 + 24) with stream-K over all 256
+    # compute units; without it, the plain choice (no stream-K)
     args = (4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
     ws = pg.workspace_f32(*args[:3])
-    v, split = pg.select_ws_f32(*args, ws)
-    assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_ua") and split == 10
+    v, sk = pg.select_ws_f32(*args, ws)
+    assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_ua") and sk == 256
     for short in (0, ws - 1):
-        v0, split0 = pg.select_ws_f32(*args, short)
-        assert v0 == pg.select_f32(*args) and split0 == 1
+        v0, sk0 = pg.select_ws_f32(*args, short)
+        assert v0 == pg.select_f32(*args) and sk0 == 0
     # shapes that fill whole rounds: same as the plain entry point
     sq = (8192, 8192, 8192, 1.5, FAKE, 8192, FAKE, 8192, 0.5, FAKE, 8192)
-    assert pg.select_ws_f32(*sq, 1 << 30) == (pg.select_f32(*sq), 1)
+    assert pg.select_ws_f32(*sq, 1 << 30) == (pg.select_f32(*sq), 0)
     d = (4096, 4096, 4096, 1.0, FAKE, 4104, FAKE, 4104, 1.0, FAKE, 4104)
-    assert pg.select_ws_f64(*d, 1 << 30) == (pg.select_f64(*d), 1)
-    # invalid arguments: the same status as the plain selector, split left at 1
+    assert pg.select_ws_f64(*d, 1 << 30) == (pg.select_f64(*d), 0)
+    # fewer workgroups than compute units where each keeps 4 K tiles: 8
+    # leftover 128 x 128 tiles of 50 K tiles -> 100
+    e = (725, 5528, 796, 1.0, FAKE, 725, FAKE, 796, 1.0, FAKE, 725)
+    v, sk = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
+    assert name_of(v).startswith("f32_128x128") and sk == 100
+    # invalid arguments: the same status as the plain selector, no stream-K
     bad = (4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4)
-    assert pg.select_ws_f32(*bad, 1 << 20) == (-6, 1)
+    assert pg.select_ws_f32(*bad, 1 << 20) == (-6, 0)
 
 
 def test_status_strings():
@@ -187,24 +192,29 @@ def test_workspace_entry_points_host_checks():
 
 
 def test_workspace_sizes():
-    # 8192^3: 1024 tiles of 256 x 256 fill whole rounds on 256 CUs -> no split
+    # 8192^3: 1024 tiles of 256 x 256 fill whole rounds on 256 CUs -> none
     assert pg.workspace_f32(8192, 8192, 8192) == 0
     assert pg.workspace_f32(2048, 2048, 2048) == 0
     assert pg.workspace_f32(0, 10, 10) == 0 and pg.workspace_f32(10, 10, 0) == 0
     # 4097 x 3001 x 1023 on 128 x 128 x 16 tiles: 33 x 24 = 792 tiles = 3
-    # rounds of 256 + 24 leftover tiles, each split into min(256 // 24, 64 // 4)
-    # = 10 slices of 6 or 7 K tiles (64 in all).  256 compute units: the
-    # MI355X, and the fallback with no GPU.
-    assert pg.workspace_f32(4097, 3001, 1023) == 24 * 10 * 128 * 128 * 4
-    # too few K tiles to split after a full round (4 per slice)
+    # rounds of 256 + 24 leftover tiles (1536 K iterations) shared by 256
+    # workgroups, two workspace slots each.  256 compute units: the MI355X,
+    # and the fallback with no GPU.
+    assert pg.workspace_f32(4097, 3001, 1023) == 2 * 256 * 128 * 128 * 4
+    # 3840^3: 900 tiles of 128^2 = 3 rounds + 132, a last round above half
+    # full, still shared
+    assert pg.workspace_f32(3840, 3840, 3840) == 2 * 256 * 128 * 128 * 4
+    assert pg.workspace_f64(3840, 3840, 3840) == 2 * 256 * 128 * 128 * 8
+    # too few K tiles to share after a full round (4 per workgroup)
     assert pg.workspace_f32(4097, 3001, 100) == 0
-    # fewer tiles than half the compute units: 512^3 is 64 tiles of 64^2,
-    # each split into 4 slices (256 / 64) of 8 K tiles of 16
-    assert pg.workspace_f32(512, 512, 512) == 64 * 4 * 64 * 64 * 4
-    # 1024^3 is one round of 256 such tiles: no split
+    # 512^3 fp32: 64 tiles of 64^2; sharing them is estimated not to pay for
+    # the fix-up kernel's launch
+    assert pg.workspace_f32(512, 512, 512) == 0
+    # 1024^3 is one round of 256 such tiles: none
     assert pg.workspace_f32(1024, 1024, 1024) == 0
-    # every tiling leaves its last round more than half full: no split
-    assert pg.workspace_f32(3840, 3840, 3840) == 0
+    # 74 x 104 x 771 fp64: 4 tiles of 64^2 with 49 K tiles, at least 2 per
+    # workgroup -> 98 workgroups
+    assert pg.workspace_f64(74, 104, 771) == 2 * 98 * 64 * 64 * 8
 
 
 def test_matmat_host_argument_codes_and_quick_returns():

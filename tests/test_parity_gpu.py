@@ -312,7 +312,7 @@ def test_concurrent_calls_on_two_streams():
     ref32 = oracle_full(p32)
     ref64 = oracle_full(p64)
     need = ws_size(p32)
-    assert need > 0, "the fp32 case should take the split path"
+    assert need > 0, "the fp32 case should take the stream-K path"
     jobs = []
     for p in (p32, p64):
         A = torch.from_numpy(p.A).cuda()
@@ -404,7 +404,7 @@ def test_python_gemm_layouts():
     assert torch.all(Ccol_store[:, 333:] == 0)
 
 
-# ------------------------------- split of the last round of tiles (workspace)
+# ------------------------- stream-K of the last round of tiles (workspace)
 def ws_size(p):
     fn = pg.workspace_f32 if p.dtype == np.float32 else pg.workspace_f64
     return fn(p.m, p.n, p.k)
@@ -431,35 +431,43 @@ def run_ws(p, ws_bytes=None):
 
 
 # (dtype, m, n, k): each leaves a partly filled last round of tiles on 256
-# compute units and so takes the split path (tiling and slices as the library
-# chooses them on 256 units); together they cover every tile class of each
-# precision, ragged M/N edges inside the split tiles and a K tail in the
-# last slice.
-SPLIT_SHAPES = [
-    (np.float32, 2053, 2048, 1000),    # 128^2 tiles: 272 = 256 + 16, 15 slices
-    (np.float32, 2100, 2000, 555),     # 128^2 tiles, 8 slices, K tail of 11
-    (np.float32, 4352, 4096, 640),     # 128^2 tiles: 1088 = 4*256 + 64, 4 slices
-    (np.float32, 8192, 4352, 640),     # 256x128 tiles: 1088 = 4*256 + 64, 4 slices
-    (np.float64, 4200, 2048, 300),     # 128^2 fp64 tiles: 528 = 2*256 + 16, 4 slices
-    (np.float64, 2100, 2000, 333),     # 64^2 fp64 tiles: 1056 = 4*256 + 32, K tail
-    # fewer tiles than half the compute units: every tile split (at least 2
-    # K tiles each)
-    (np.float32, 512, 512, 512),       # 64 tiles of 64^2 x 4 slices
-    (np.float32, 300, 200, 1000),      # 20 edge tiles x 12 slices
-    (np.float64, 200, 130, 333),       # 12 fp64 edge tiles x 10 slices, K tail
-    (np.float32, 128, 128, 128),       # 4 tiles x 4 slices of 2 K tiles
+# compute units and so takes the stream-K path (tiling and plan as the
+# library chooses them on 256 units: R full rounds + the rest, S stream-K
+# workgroups of I iterations, "crossing": ranges that span two tiles).
+# Together they cover every tile class with a stream-K form, last rounds
+# below and above half full, no full round at all, ranges aligned with the
+# tiles or crossing them, ragged M/N edges and K tails inside the shared
+# tiles, fewer workgroups than compute units, and up to 43 pieces summed
+# per tile.
+SK_SHAPES = [
+    (np.float32, 2053, 2048, 1000),    # 128^2: 256 + 16, S 252, I 4, crossing, K tail 8
+    (np.float32, 4285, 2022, 736),     # 128^2: 2*256 + 32, I 5-6, 8 aligned pieces a tile
+    (np.float32, 725, 5528, 796),      # 128^2: 256 + 8, S 100, crossing, K tail 12
+    (np.float32, 1743, 3551, 988),     # 128^2: 256 + 136, I 32-33, crossing, K tail 12
+    (np.float32, 2782, 1093, 2321),    # 128^2: 198 tiles and no full round, K tail 1
+    (np.float64, 1647, 3928, 1267),    # fp64 128^2: 256 + 147, crossing, K tail 3
+    (np.float64, 2073, 2039, 832),     # fp64 128^2: 256 + 16, S 208, aligned
+    (np.float64, 1619, 5039, 519),     # fp64 128^2: 2*256 + 8, S 66, crossing, K tail 7
+    (np.float32, 4121, 344, 2015),     # 64^2: 256 + 134, I 65-66, crossing, K tail 15
+    (np.float64, 264, 4934, 1341),     # fp64 64^2: 256 + 134, crossing, K tail 13
+    (np.float64, 284, 3284, 656),      # fp64 64^2: 256 + 4, S 41, crossing
+    # no full round: every tile shared (at least 2 K tiles per workgroup)
+    (np.float32, 255, 140, 819),       # 12 edge tiles of 64^2, I 2-3, K tail 3
+    (np.float32, 70, 163, 913),        # 6 edge tiles, S 174, 29 aligned pieces, K tail 1
+    (np.float32, 130, 70, 2000),       # 6 edge tiles, 43 pieces each, I 2-3
+    (np.float64, 74, 104, 771),        # 4 fp64 edge tiles, S 98, crossing, K tail 3
 ]
 
 
-@pytest.mark.parametrize("case", range(len(SPLIT_SHAPES)))
-def test_split_exact_integer(case):
-    dtype, m, n, k = SPLIT_SHAPES[case]
+@pytest.mark.parametrize("case", range(len(SK_SHAPES)))
+def test_stream_k_exact_integer(case):
+    dtype, m, n, k = SK_SHAPES[case]
     alpha, beta = ALPHA_BETA[case % len(ALPHA_BETA)]
     chunk = 4 if dtype == np.float32 else 2
     lds = leading_dims(m, k, case % 2 == 0, chunk, case)
     p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=300 + case)
-    assert ws_size(p) > 0, "shape no longer takes the split path"
-    say("split", np.dtype(dtype).name, (m, n, k), (alpha, beta), "ld", lds, "ws", ws_size(p))
+    assert ws_size(p) > 0, "shape no longer takes the stream-K path"
+    say("stream-K", np.dtype(dtype).name, (m, n, k), (alpha, beta), "ld", lds, "ws", ws_size(p))
     C = run_ws(p)
     assert_bitwise(C, oracle_full(p))
 
@@ -487,8 +495,8 @@ def _random_cases(count, seed, mn_range=(1, 900), k_range=(1, 700)):
     return cases
 
 
-# small shapes (the 64 x 64 classes, most with the split of every tile) and
-# mid-sized ones (every tile class, splits of a last round)
+# small shapes (the 64 x 64 classes, most with stream-K over every tile) and
+# mid-sized ones (every tile class, stream-K of a last round)
 RANDOM_CASES = (_random_cases(48, seed=2024)
                 + _random_cases(16, seed=2025, mn_range=(900, 2600), k_range=(1, 1200)))
 
@@ -496,7 +504,7 @@ RANDOM_CASES = (_random_cases(48, seed=2024)
 @pytest.mark.parametrize("case", range(len(RANDOM_CASES)))
 def test_random_shapes_every_entry_exact_integer(case):
     """The default entry point (whatever tile class its model picks) and the
-    workspace entry point (with the split it asks for) on seeded random small
+    workspace entry point (with the stream-K plan it asks for) on seeded random small
     shapes, aligned or odd leading dimensions: bitwise equal to the oracle on
     exact-integer inputs, padding and guard bands untouched."""
     dtype, m, n, k, lds, alpha, beta = RANDOM_CASES[case]
@@ -532,25 +540,25 @@ def test_random_shapes_long():
             say("long random", t, np.dtype(dtype).name, (m, n, k), lds, (alpha, beta))
 
 
-def test_split_ragged_workload_parity():
+def test_stream_k_ragged_workload_parity():
     p = gi.workload("sgemm_ragged")
     assert ws_size(p) > 0
     C = run_ws(p)
     maxabs, rel = assert_f32_parity(C, oracle_full(p), p.k)
-    say("ragged split max|dC| %.3g rel %.3g" % (maxabs, rel))
+    say("ragged stream-K max|dC| %.3g rel %.3g" % (maxabs, rel))
     q = gi.workload("sgemm_ragged", dist_override="i2")
     assert_bitwise(run_ws(q), oracle_full(q))
 
 
-def test_split_fp64_parity():
-    p = gi.make_colmajor_problem("split64", np.float64, 2100, 2000, 333, 2101, 333, 2103,
+def test_stream_k_fp64_parity():
+    p = gi.make_colmajor_problem("sk64", np.float64, 1647, 3928, 1267, 1649, 1267, 1651,
                                  0.75, -1.25, seed=31, dist="n", c_dist="n")
     assert ws_size(p) > 0
     assert_f64_parity(run_ws(p), oracle_full(p))
 
 
-def test_split_deterministic_and_small_workspace_is_plain():
-    p = gi.make_colmajor_problem("splitdet", np.float32, 2053, 2048, 1000, 2053, 1000, 2053,
+def test_stream_k_deterministic_and_small_workspace_is_plain():
+    p = gi.make_colmajor_problem("skdet", np.float32, 2053, 2048, 1000, 2053, 1000, 2053,
                                  1.5, 0.5, seed=32, dist="u", c_dist="u")
     need = ws_size(p)
     C1, C2 = run_ws(p), run_ws(p)
