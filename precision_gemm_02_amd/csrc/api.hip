@@ -140,29 +140,92 @@ int device_cus() {
 
 // Stream-K for the last round of tiles.  With T tiles on P compute units,
 // the first R = floor(T/P) rounds stay one tile per workgroup; the K tiles of
-// the remaining Tr = T - R*P tiles (I = Tr*nk iterations) are shared evenly
-// by S more workgroups, S <= P and S > Tr so that tiles are shared, each
-// taking at least 4 K tiles after a full round (the shared tiles then run
-// beside nothing else) or 2 without one (small problems).  A workgroup's
-// range covers the end of one tile and the start of the next at most; each
-// piece's partial sums go to the workspace (two slots per workgroup) and the
-// fix-up kernel adds each tile's pieces in K order.
+// the remaining Tr = T - R*P tiles (I = Tr*nk iterations, in (tile, K tile)
+// order) are shared by S more workgroups, workgroup w taking iterations
+// [floor(w*I/S), floor((w+1)*I/S)).  S > Tr, so a range is shorter than a
+// tile and covers the end of one tile and the start of the next at most;
+// each piece's partial sums go to the workspace (two slots per workgroup)
+// and the fix-up kernel adds each tile's pieces in K order.  Every range
+// keeps at least 4 K tiles after a full round (the shared tiles then run
+// beside nothing else) or 2 without one (small problems).  Two values of S
+// are weighed: as many workgroups as that allows, up to P, or a multiple of
+// Tr (s workgroups per tile, up to P), whose ranges never cross a tile, so
+// each workgroup runs one piece.
 struct SkPlan {
   int full_tiles = 0, wgs = 0;
   size_t bytes = 0;
 };
 
+// Whether some range of S workgroups over I = tr*nk iterations crosses a
+// tile boundary (then some workgroups run two pieces).  Boundary j*nk starts
+// a range iff some w has j*S/tr <= w < j*S/tr + S/I: with x = j*S mod tr,
+// iff x == 0 or (tr - x)*nk < S.
+inline bool sk_crosses(long long tr, long long nk, long long S) {
+  if (S % tr == 0) return false;
+  for (long long j = 1; j < tr; ++j) {
+    const long long x = (j * S) % tr;
+    if (x != 0 && (tr - x) * nk >= S) return true;
+  }
+  return false;
+}
+
+// Estimated time of the last round under stream-K with S workgroups (same
+// units and fixed part as estimate below): the longest range's share of a
+// tile's K loop, the fixed part of one or two pieces, and the fix-up kernel
+// (its HBM traffic at ~4 TB/s and ~8 us for its launch behind the GEMM
+// kernel and the uneven end of the pieces, fitted to 29 measured shapes).
 template <typename T>
-SkPlan sk_plan(const Variant<T>& v, int m, int n, int k, int cus) {
+double sk_time(const Variant<T>& v, double kloop, double fixed, long long tr, long long nk,
+               long long S, double unit_s) {
+  const long long per_wg = ceil_div(tr * nk, S);
+  const double tile_bytes = (double)v.bm * v.bn * sizeof(T);
+  const double fix_bytes = ((double)S + 3.0 * (double)tr) * tile_bytes;
+  return kloop * (double)per_wg / (double)nk + (sk_crosses(tr, nk, S) ? 2 : 1) * fixed +
+         (fix_bytes / 4e12 + 8e-6) / unit_s;
+}
+
+// Per-precision constants of the time model: one multiply-add on one compute
+// unit at the precision's matrix peak, in seconds.
+template <typename T>
+constexpr double unit_seconds() {
+  return 2.0 / ((sizeof(T) == 4 ? 157.3e12 : 78.6e12) / 256);
+}
+
+// A tile's K loop at efficiency eff, and the fixed part of a round: ~1.5 us
+// of prologue and the round's stores of C at ~5 TB/s (both in units).
+template <typename T>
+void round_costs(const Variant<T>& v, double eff, int k, int cus, double* kloop, double* fixed) {
+  const double c_bytes = (double)cus * v.bm * v.bn * sizeof(T);
+  *kloop = (double)v.bm * (double)v.bn * (double)k / eff;
+  *fixed = (1.5e-6 + c_bytes / 5e12) / unit_seconds<T>();
+}
+
+template <typename T>
+SkPlan sk_plan(const Variant<T>& v, double eff, int m, int n, int k, int cus) {
   SkPlan p;
   const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
   const long long nk = ceil_div(k, v.bk);
   if (rest == 0) return p;
   const long long min_iters = rounds >= 1 ? 4 : 2;
-  long long S = rest * nk / min_iters;
-  if (S > cus) S = cus;
-  if (S <= rest) return p;
+  long long s_all = rest * nk / min_iters;
+  if (s_all > cus) s_all = cus;
+  long long per_tile = cus / rest;
+  if (per_tile > nk / min_iters) per_tile = nk / min_iters;
+  const long long s_al = rest * per_tile;
+  double kloop, fixed;
+  round_costs(v, eff, k, cus, &kloop, &fixed);
+  long long S = 0;
+  double best = 0;
+  for (const long long c : {s_al, s_all}) {
+    if (c <= rest) continue;
+    const double t = sk_time(v, kloop, fixed, rest, nk, c, unit_seconds<T>());
+    if (S == 0 || t < best) {
+      S = c;
+      best = t;
+    }
+  }
+  if (S == 0) return p;
   p.full_tiles = (int)(rounds * cus);
   p.wgs = (int)S;
   p.bytes = (size_t)2 * (size_t)S * (size_t)v.bm * (size_t)v.bn * sizeof(T);
@@ -172,40 +235,22 @@ SkPlan sk_plan(const Variant<T>& v, int m, int n, int k, int cus) {
 // Estimated time of variant v on an m x n x k problem, in multiply-adds of
 // one compute unit at the precision's full matrix rate.  Each round of tiles
 // (every compute unit busy with one tile) costs the tile's K loop at the
-// class's efficiency plus a fixed part: ~1.5 us of prologue and the round's
-// stores of C at ~5 TB/s.  The last, partly filled round costs a whole
-// round, or with stream-K (`sk`) each workgroup's share of its K iterations,
-// the fixed part of one or two pieces and the fix-up kernel (its HBM
-// traffic at ~4 TB/s and ~8 us for its launch behind the GEMM kernel and the
-// uneven end of the pieces, fitted to 29 measured shapes).  Edge tiles cost
-// as much as inner ones (they run the same loop).  On 20 fp32 shapes from
-// 512^3 to 12000 x 2000 x 4000 and 9 fp64 sizes the plain estimate picks the
-// fastest tile class (within 1 %).
+// class's efficiency plus the fixed part (round_costs).  The last, partly
+// filled round costs a whole round, or with a stream-K plan (`sk`) its
+// sk_time.  Edge tiles cost as much as inner ones (they run the same loop).  On
+// 20 fp32 shapes from 512^3 to 12000 x 2000 x 4000 and 9 fp64 sizes the
+// plain estimate picks the fastest tile class (within 1 %).
 template <typename T>
-double estimate(const Variant<T>& v, double eff, int m, int n, int k, int cus, bool sk) {
-  // one multiply-add on one compute unit at the precision's matrix peak
-  const double unit_s = 2.0 / ((sizeof(T) == 4 ? 157.3e12 : 78.6e12) / 256);
+double estimate(const Variant<T>& v, double eff, int m, int n, int k, int cus,
+                const SkPlan* sk) {
   const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
-  const double c_bytes = (double)cus * v.bm * v.bn * sizeof(T);
-  const double kloop = (double)v.bm * (double)v.bn * (double)k / eff;
-  const double fixed = (1.5e-6 + c_bytes / 5e12) / unit_s;
+  double kloop, fixed;
+  round_costs(v, eff, k, cus, &kloop, &fixed);
   const double t = (double)rounds * (kloop + fixed);
   if (rest == 0) return t;
-  if (sk) {
-    const SkPlan p = sk_plan(v, m, n, k, cus);
-    if (p.wgs > 0) {
-      const long long nk = ceil_div(k, v.bk), iters = rest * nk;
-      const long long per_wg = ceil_div(iters, p.wgs);
-      // two pieces (two prologues and epilogues) unless every range lies
-      // inside one tile
-      const bool aligned = iters % p.wgs == 0 && nk % per_wg == 0;
-      const double tile_bytes = (double)v.bm * v.bn * sizeof(T);
-      const double fix_bytes = ((double)p.wgs + 3.0 * (double)rest) * tile_bytes;
-      return t + kloop * (double)per_wg / (double)nk + (aligned ? 1 : 2) * fixed +
-             (fix_bytes / 4e12 + 8e-6) / unit_s;
-    }
-  }
+  if (sk != nullptr && sk->wgs > 0)
+    return t + sk_time(v, kloop, fixed, rest, ceil_div(k, v.bk), sk->wgs, unit_seconds<T>());
   return t + kloop + fixed;
 }
 
@@ -237,12 +282,13 @@ Choice choose(int m, int n, int k, bool sk_ok) {
   double best_t = 0;
   for (int c = 0; c < ncls; ++c) {
     const Variant<T>& v = table[cls[c].vec];
-    double e = estimate(v, cls[c].eff, m, n, k, cus, false);
+    double e = estimate(v, cls[c].eff, m, n, k, cus, nullptr);
     bool sk = false;
-    if (sk_ok && v.sk && sk_plan(v, m, n, k, cus).wgs > 0) {
+    const SkPlan p = (sk_ok && v.sk) ? sk_plan(v, cls[c].eff, m, n, k, cus) : SkPlan{};
+    if (p.wgs > 0) {
       // stream-K only where it is estimated at least 1 % faster: below that
       // the measured gains were within noise or losses
-      const double e_sk = estimate(v, cls[c].eff, m, n, k, cus, true);
+      const double e_sk = estimate(v, cls[c].eff, m, n, k, cus, &p);
       if (e_sk * 1.01 < e) {
         e = e_sk;
         sk = true;
@@ -275,7 +321,7 @@ int pick(int m, int n, int k, bool vec, size_t ws_bytes, SkPlan* plan) {
   if (ws_bytes > 0) {
     const Choice c = choose<T>(m, n, k, true);
     if (c.sk) {
-      const SkPlan p = sk_plan(table[cls[c.cls].vec], m, n, k, device_cus());
+      const SkPlan p = sk_plan(table[cls[c.cls].vec], cls[c.cls].eff, m, n, k, device_cus());
       if (ws_bytes >= p.bytes) {
         *plan = p;
         return vec ? cls[c.cls].vec : cls[c.cls].ua;
@@ -369,9 +415,9 @@ size_t workspace_impl(int m, int n, int k) {
   if (!c.sk) return 0;
   // the aligned and unaligned variants of a tile class share their tiling
   if constexpr (sizeof(T) == 4)
-    return sk_plan(t.f32[t.f32c[c.cls].vec], m, n, k, device_cus()).bytes;
+    return sk_plan(t.f32[t.f32c[c.cls].vec], t.f32c[c.cls].eff, m, n, k, device_cus()).bytes;
   else
-    return sk_plan(t.f64[t.f64c[c.cls].vec], m, n, k, device_cus()).bytes;
+    return sk_plan(t.f64[t.f64c[c.cls].vec], t.f64c[c.cls].eff, m, n, k, device_cus()).bytes;
 }
 
 template <typename T>

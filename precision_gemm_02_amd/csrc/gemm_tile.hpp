@@ -980,9 +980,11 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
 // Fix-up of the stream-K tiles: C = alpha * (sum of the pieces' partial
 // sums, in K order) + beta * C for every element of the remaining tiles that
 // lies inside C.  Tile r's pieces come from the stream-K workgroups whose
-// iteration ranges meet [r*nk, (r+1)*nk): workgroup w's piece is its slot 2w
-// if its range starts in tile r, 2w + 1 if it started in tile r - 1.  One
-// thread per element; block y = remaining tile.
+// iteration ranges [b(w), b(w+1)), b(w) = floor(w*I/P), meet [r*nk,
+// (r+1)*nk): workgroup w's piece is its slot 2w if its range starts in tile
+// r, 2w + 1 if it started in tile r - 1.  One thread per element; block y =
+// remaining tile.  The walk over w is the same for the whole block and
+// steps b(w) by I/P with a remainder, without a division per step.
 template <typename T>
 __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs<T> g, int bm, int bn, int bk) {
   const int r = blockIdx.y;
@@ -996,16 +998,38 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs<T> g, int bm, in
   const long long rest = (long long)g.tiles_m * g.tiles_n - g.full_tiles;
   const long long iters = rest * nk, P = g.sk_wgs;
   const long long lo = (long long)r * nk, hi = lo + nk;
-  // b(w) = w*iters/P; the first workgroup whose range ends past lo
+  const long long dq = iters / P, dr = iters % P;
+  // w with b(w) <= lo, then b(w) = q and (w*I) mod P = rm
   long long w = (lo * P) / iters;
-  while (w > 0 && (w * iters) / P > lo) --w;
-  while (((w + 1) * iters) / P <= lo) ++w;
+  long long q = (w * iters) / P, rm = (w * iters) % P;
+  // b(w+1) from b(w)
+  long long q1 = q + dq, rm1 = rm + dr;
+  if (rm1 >= P) {
+    ++q1;
+    rm1 -= P;
+  }
+  // first workgroup whose range ends past lo
+  while (q1 <= lo) {
+    ++w;
+    q = q1;
+    rm = rm1;
+    q1 = q + dq;
+    rm1 = rm + dr;
+    if (rm1 >= P) {
+      ++q1;
+      rm1 -= P;
+    }
+  }
   const size_t slot = (size_t)bm * bn;
   T sum = T(0);
-  for (; w < P && (w * iters) / P < hi; ++w) {
-    const long long b = (w * iters) / P;
-    const int piece = (b >= lo) ? 0 : 1;
-    sum += g.ws[(size_t)(2 * w + piece) * slot + e];
+  for (; w < P && q < hi; ++w) {
+    sum += g.ws[(size_t)(2 * w + (q >= lo ? 0 : 1)) * slot + e];
+    q += dq;
+    rm += dr;
+    if (rm >= P) {
+      ++q;
+      rm -= P;
+    }
   }
   T* pc = g.C + (size_t)j * g.ldc + i;
   T v = g.alpha * sum;

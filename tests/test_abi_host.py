@@ -142,12 +142,13 @@ def test_selection_by_shape_and_alignment():
 
 def test_selection_with_workspace():
     # the ragged 4097 x 3001 x 1023 problem: with the workspace it asks for,
-    # 128 x 128 tiles (3 full rounds of 256 + 24) with stream-K over all 256
-    # compute units; without it, the plain choice (no stream-K)
+    # 128 x 128 tiles (3 full rounds of 256 + 24) with 240 stream-K
+    # workgroups (10 per leftover tile: no range crosses a tile); without
+    # it, the plain choice (no stream-K)
     args = (4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
     ws = pg.workspace_f32(*args[:3])
     v, sk = pg.select_ws_f32(*args, ws)
-    assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_ua") and sk == 256
+    assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_ua") and sk == 240
     for short in (0, ws - 1):
         v0, sk0 = pg.select_ws_f32(*args, short)
         assert v0 == pg.select_f32(*args) and sk0 == 0
@@ -156,11 +157,16 @@ def test_selection_with_workspace():
     assert pg.select_ws_f32(*sq, 1 << 30) == (pg.select_f32(*sq), 0)
     d = (4096, 4096, 4096, 1.0, FAKE, 4104, FAKE, 4104, 1.0, FAKE, 4104)
     assert pg.select_ws_f64(*d, 1 << 30) == (pg.select_f64(*d), 0)
-    # fewer workgroups than compute units where each keeps 4 K tiles: 8
-    # leftover 128 x 128 tiles of 50 K tiles -> 100
+    # 8 leftover 128 x 128 tiles of 50 K tiles: 12 workgroups per tile (each
+    # keeps at least 4 K tiles) -> 96, no range crossing a tile
     e = (725, 5528, 796, 1.0, FAKE, 725, FAKE, 796, 1.0, FAKE, 725)
     v, sk = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
-    assert name_of(v).startswith("f32_128x128") and sk == 100
+    assert name_of(v).startswith("f32_128x128") and sk == 96
+    # 136 leftover tiles (above half the units): all 256 units, ranges of
+    # 32-33 K tiles that cross tiles
+    e = (1743, 3551, 988, 1.0, FAKE, 1743, FAKE, 988, 1.0, FAKE, 1743)
+    v, sk = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
+    assert name_of(v).startswith("f32_128x128") and sk == 256
     # invalid arguments: the same status as the plain selector, no stream-K
     bad = (4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4)
     assert pg.select_ws_f32(*bad, 1 << 20) == (-6, 0)
@@ -197,10 +203,10 @@ def test_workspace_sizes():
     assert pg.workspace_f32(2048, 2048, 2048) == 0
     assert pg.workspace_f32(0, 10, 10) == 0 and pg.workspace_f32(10, 10, 0) == 0
     # 4097 x 3001 x 1023 on 128 x 128 x 16 tiles: 33 x 24 = 792 tiles = 3
-    # rounds of 256 + 24 leftover tiles (1536 K iterations) shared by 256
+    # rounds of 256 + 24 leftover tiles (64 K tiles each) shared by 240
     # workgroups, two workspace slots each.  256 compute units: the MI355X,
     # and the fallback with no GPU.
-    assert pg.workspace_f32(4097, 3001, 1023) == 2 * 256 * 128 * 128 * 4
+    assert pg.workspace_f32(4097, 3001, 1023) == 2 * 240 * 128 * 128 * 4
     # 3840^3: 900 tiles of 128^2 = 3 rounds + 132, a last round above half
     # full, still shared
     assert pg.workspace_f32(3840, 3840, 3840) == 2 * 256 * 128 * 128 * 4
@@ -212,9 +218,9 @@ def test_workspace_sizes():
     assert pg.workspace_f32(512, 512, 512) == 0
     # 1024^3 is one round of 256 such tiles: none
     assert pg.workspace_f32(1024, 1024, 1024) == 0
-    # 74 x 104 x 771 fp64: 4 tiles of 64^2 with 49 K tiles, at least 2 per
-    # workgroup -> 98 workgroups
-    assert pg.workspace_f64(74, 104, 771) == 2 * 98 * 64 * 64 * 8
+    # 74 x 104 x 771 fp64: 4 tiles of 64^2 with 49 K tiles, 24 workgroups per
+    # tile (at least 2 K tiles each) -> 96 workgroups
+    assert pg.workspace_f64(74, 104, 771) == 2 * 96 * 64 * 64 * 8
 
 
 def test_matmat_host_argument_codes_and_quick_returns():

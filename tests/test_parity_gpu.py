@@ -433,29 +433,31 @@ def run_ws(p, ws_bytes=None):
 # (dtype, m, n, k): each leaves a partly filled last round of tiles on 256
 # compute units and so takes the stream-K path (tiling and plan as the
 # library chooses them on 256 units: R full rounds + the rest, S stream-K
-# workgroups of I iterations, "crossing": ranges that span two tiles).
-# Together they cover every tile class with a stream-K form, last rounds
-# below and above half full, no full round at all, ranges aligned with the
-# tiles or crossing them, ragged M/N edges and K tails inside the shared
-# tiles, fewer workgroups than compute units, and up to 43 pieces summed
-# per tile.
+# workgroups of I iterations; "aligned": S is a multiple of the shared tiles
+# and no range crosses a tile; "crossing": some workgroups run two pieces).
+# Together they cover every tile class with a stream-K form in both
+# precisions, last rounds below and above half full and no full round at
+# all, aligned and crossing plans, fewer workgroups than compute units,
+# ragged M/N edges and K tails inside the shared tiles, and up to 42 pieces
+# summed per tile.
 SK_SHAPES = [
-    (np.float32, 2053, 2048, 1000),    # 128^2: 256 + 16, S 252, I 4, crossing, K tail 8
-    (np.float32, 4285, 2022, 736),     # 128^2: 2*256 + 32, I 5-6, 8 aligned pieces a tile
-    (np.float32, 725, 5528, 796),      # 128^2: 256 + 8, S 100, crossing, K tail 12
+    (np.float32, 2053, 2048, 1000),    # 128^2: 256 + 16, S 240 aligned, K tail 8
+    (np.float32, 725, 5528, 796),      # 128^2: 256 + 8, S 96 aligned, K tail 12
+    (np.float32, 1134, 4856, 1042),    # 128^2: 256 + 86, I 22-23, crossing, K tail 2
     (np.float32, 1743, 3551, 988),     # 128^2: 256 + 136, I 32-33, crossing, K tail 12
-    (np.float32, 2782, 1093, 2321),    # 128^2: 198 tiles and no full round, K tail 1
-    (np.float64, 1647, 3928, 1267),    # fp64 128^2: 256 + 147, crossing, K tail 3
-    (np.float64, 2073, 2039, 832),     # fp64 128^2: 256 + 16, S 208, aligned
-    (np.float64, 1619, 5039, 519),     # fp64 128^2: 2*256 + 8, S 66, crossing, K tail 7
+    (np.float64, 2812, 2428, 1238),    # fp64 128^2: 256 + 162, crossing, K tail 6
+    (np.float64, 3789, 3267, 211),     # fp64 128^2: 3*256 + 12, S 36 aligned, K tail 3
+    (np.float64, 2398, 2258, 1304),    # fp64 128^2: 256 + 86, crossing, K tail 8
     (np.float32, 4121, 344, 2015),     # 64^2: 256 + 134, I 65-66, crossing, K tail 15
     (np.float64, 264, 4934, 1341),     # fp64 64^2: 256 + 134, crossing, K tail 13
-    (np.float64, 284, 3284, 656),      # fp64 64^2: 256 + 4, S 41, crossing
+    (np.float64, 284, 3284, 656),      # fp64 64^2: 256 + 4, S 40 aligned
     # no full round: every tile shared (at least 2 K tiles per workgroup)
-    (np.float32, 255, 140, 819),       # 12 edge tiles of 64^2, I 2-3, K tail 3
-    (np.float32, 70, 163, 913),        # 6 edge tiles, S 174, 29 aligned pieces, K tail 1
-    (np.float32, 130, 70, 2000),       # 6 edge tiles, 43 pieces each, I 2-3
-    (np.float64, 74, 104, 771),        # 4 fp64 edge tiles, S 98, crossing, K tail 3
+    (np.float32, 68, 2807, 1579),      # 88 edge tiles of 64^2, I 34-35, crossing
+    (np.float64, 3009, 87, 1029),      # 96 fp64 edge tiles, crossing, K tail 5
+    (np.float32, 255, 140, 819),       # 12 edge tiles, S 252 aligned, K tail 3
+    (np.float32, 70, 163, 913),        # 6 edge tiles, S 174, 29 pieces each, K tail 1
+    (np.float32, 130, 70, 2000),       # 6 edge tiles, 42 pieces each, I 2-3
+    (np.float64, 74, 104, 771),        # 4 fp64 edge tiles, S 96 aligned, K tail 3
 ]
 
 
@@ -551,7 +553,7 @@ def test_stream_k_ragged_workload_parity():
 
 
 def test_stream_k_fp64_parity():
-    p = gi.make_colmajor_problem("sk64", np.float64, 1647, 3928, 1267, 1649, 1267, 1651,
+    p = gi.make_colmajor_problem("sk64", np.float64, 2812, 2428, 1238, 2813, 1238, 2815,
                                  0.75, -1.25, seed=31, dist="n", c_dist="n")
     assert ws_size(p) > 0
     assert_f64_parity(run_ws(p), oracle_full(p))
