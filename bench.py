@@ -224,15 +224,29 @@ def recorded_counters(variant: str, workload: str):
             "source": "rocprofv3 --pmc, profiles/ (same built library)"}
 
 
+def device_peak(dt: str):
+    """(matrix peak in TFLOP/s from the device's own compute-unit count and
+    peak clock, CUs, clock MHz): 256 flop per CU per cycle for fp32, 128 for
+    fp64 (the published peaks are these at 256 CUs and 2.4 GHz)."""
+    import precision_gemm_02_amd as pg
+    cus, khz = pg.device_info()
+    per_cycle = 256 if dt == "f32" else 128
+    return cus * khz * 1e3 * per_cycle / 1e12, cus, khz / 1e3
+
+
 def roofline(r: Resident, kern_ms: list):
     """Matrix-core roofline of the GEMM kernel: achieved flops per launch over
     the mean of the per-launch event times (the median and the minimum are
-    reported beside it)."""
+    reported beside it).  `peak` is the published one; the peak recomputed
+    from the device's properties is given beside it."""
     kern_ms_mean = float(np.mean(kern_ms))
     achieved = r.flops / (kern_ms_mean * 1e-3) / 1e12
     peak = PEAK_TFLOPS[r.dt]
+    dpeak, cus, mhz = device_peak(r.dt)
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
+            "peak_device_props": round(dpeak, 2), "frac_device_props": round(achieved / dpeak, 4),
+            "device": {"cus": cus, "clock_mhz": mhz},
             "traffic": recorded_traffic(r.variant, r.name),
             "counters": recorded_counters(r.variant, r.name),
             "algorithmic_bytes": r.algorithmic_bytes(),
@@ -285,6 +299,10 @@ def sweep(args):
     oracle.build(force=False)
     cores = oracle.num_threads()
     rows = []
+    # written between the launches of the cold-cache timing: twice the
+    # 256 MB MALL, so no operand survives in any cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    one_thread = {}
     for name in gi.WORKLOADS:
         log("sweep", name)
         r = Resident(name)
@@ -300,6 +318,7 @@ def sweep(args):
         r.reset_c()
         _, kern_ms, _ = time_workload(r, max(args.steps, 10), args.warmup,
                                           args.min_warmup_seconds)
+        cold_ms = cold_kernel_ms(r, flush, 5)
         cols = p.n if p.m * p.n * p.k <= 4096 ** 3 else 512
         t0 = time.perf_counter()
         if p.rowmajor:
@@ -308,6 +327,13 @@ def sweep(args):
             R = oracle.gemm(p.m, cols, p.k, p.alpha, p.A, p.lda, p.B, p.ldb, p.beta, p.C,
                             p.ldc, dtype=p.dtype)
         t_or = time.perf_counter() - t0
+        if name in ONE_THREAD_WORKLOADS:
+            oracle.set_num_threads(1)
+            t1 = time.perf_counter()
+            oracle.gemm(p.m, cols, p.k, p.alpha, p.A, p.lda, p.B, p.ldb, p.beta, p.C, p.ldc,
+                        dtype=p.dtype)
+            one_thread[name] = time.perf_counter() - t1
+            oracle.set_num_threads(cores)
         D = got[:, :cols] - R
         maxabs = float(np.max(np.abs(D)))
         rel = float(np.linalg.norm(D) / np.linalg.norm(R))
@@ -320,22 +346,54 @@ def sweep(args):
         tflops = r.flops / (kern_med * 1e-3) / 1e12
         rows.append((name, "%dx%dx%d" % (p.m, p.n, p.k), r.entry, r.variant, kern_med, tflops,
                      100 * tflops / PEAK_TFLOPS[r.dt], cnt, maxabs, rel, ok, t_or, cols, p.n,
-                     2.0 * p.m * cols * p.k / t_or / 1e9))
+                     2.0 * p.m * cols * p.k / t_or / 1e9, cold_ms,
+                     100 * tflops / device_peak(r.dt)[0]))
         del r
         torch.cuda.empty_cache()
     print("| workload | M×N×K | entry, variant | kernel ms (median) | TFLOP/s | %% of peak "
-          "| MfmaUtil | LDS bank conflicts | max\\|ΔC\\| | rel. Frobenius | parity "
-          "| oracle s (%d threads) | oracle GFLOP/s |" % cores)
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+          "(device props) | cold-cache ms | MfmaUtil | LDS bank conflicts | max\\|ΔC\\| "
+          "| rel. Frobenius | parity | oracle s (%d threads) | oracle GFLOP/s |" % cores)
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for (name, shape, entry, var, ms, tf, pct, cnt, maxabs, rel, ok, t_or, cols, n,
-         ogf) in rows:
+         ogf, cold, dpct) in rows:
         mu = "%.1f %%" % (100 * cnt["mfma_util"]) if cnt else "—"
         lc = "%d" % cnt["lds_bank_conflict_cycles"] if cnt else "—"
         part = "" if cols == n else " (first %d of %d columns)" % (cols, n)
-        print("| %s | %s | `%s`, %s | %.4f | %.1f | %.1f | %s | %s | %.3g | %.3g | %s | %.2f%s "
-              "| %.1f |" % (name, shape, entry, var, ms, tf, pct, mu, lc, maxabs, rel,
-                            "pass" if ok else "FAIL", t_or, part, ogf))
+        print("| %s | %s | `%s`, %s | %.4f | %.1f | %.1f (%.1f) | %.4f | %s | %s | %.3g | %.3g "
+              "| %s | %.2f%s | %.1f |" % (name, shape, entry, var, ms, tf, pct, dpct, cold, mu,
+                                          lc, maxabs, rel, "pass" if ok else "FAIL", t_or,
+                                          part, ogf))
+    dpeak, cus, mhz = device_peak("f32")
+    print("\nDevice properties: %d compute units at %.0f MHz, fp32 matrix peak %.1f TFLOP/s "
+          "(fp64 %.1f)." % (cus, mhz, dpeak, dpeak / 2))
+    for name, t1 in one_thread.items():
+        p = gi.workload(name)
+        print("Oracle on 1 thread, %s: %.3f s (%.2f GFLOP/s)." %
+              (name, t1, 2.0 * p.m * p.n * p.k / t1 / 1e9))
     sys.stdout.flush()
+
+
+# workloads whose oracle is also timed on one thread (for scale)
+ONE_THREAD_WORKLOADS = ("sgemm_128", "sgemm_2048")
+
+
+def cold_kernel_ms(r: Resident, flush, launches: int) -> float:
+    """Median kernel time with cold caches: before each launch, outside its
+    pair of HIP events, C is restored (beta != 0) and a 512 MiB buffer is
+    written, which evicts the operands from L2 and the MALL."""
+    import torch
+    times = []
+    for t in range(launches):
+        r.reset_c()
+        flush.fill_(t & 0xFF)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(r.stream)
+        r.launch()
+        e.record(r.stream)
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    r.reset_c()
+    return float(np.median(times))
 
 
 def main():

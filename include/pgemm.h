@@ -194,6 +194,11 @@ int pgemm_select_ws_f64(int m, int n, int k, double alpha, const double *A, int 
                         size_t ws_bytes, int *sk_wgs);
 const char *pgemm_variant_name(int variant);
 int pgemm_num_variants(void);
+/* The current device's compute units and peak clock (kHz), as the HIP
+ * runtime reports them: the matrix peaks are cus * clock * 256 flop per
+ * cycle (fp32) and * 128 (fp64).  Returns 0, -1 / -2 for a NULL argument,
+ * or PGEMM_EHIP when no device answers. */
+int pgemm_device_info(int *cus, int *clock_khz);
 int gemm_f32_variant(int variant, int m, int n, int k, float alpha, const float *A,
                      int lda, const float *B, int ldb, float beta, float *C, int ldc,
                      void *stream);

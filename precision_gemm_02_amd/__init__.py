@@ -13,8 +13,9 @@ the layout from their strides: a column-major view (stride (1, ld)) is used
 as is; a row-major tensor (stride (ld, 1)) is served by the operand swap
 C^T = B^T A^T, which moves no data.
 
-The library must be built (``python -m precision_gemm_02_amd.build``); if it
-is missing, importing this package raises ImportError.  There is no CPU or
+The library must be built (``python precision_gemm_02_amd/build.py``, which
+does not import this package); if it is missing or older than this binding,
+importing this package raises ImportError.  There is no CPU or
 eager fallback.
 """
 from __future__ import annotations
@@ -26,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpgemm.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libpgemm.so is not built; run `python -m precision_gemm_02_amd.build` "
+    raise ImportError("libpgemm.so is not built; run `python precision_gemm_02_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 # PyTorch-ROCm ships its own HIP runtime with the same SONAME as the system
@@ -55,6 +56,18 @@ if len(_hip_runtimes_mapped()) > 1:
                       "anything that loads /opt/rocm's libamdhip64" %
                       ", ".join(sorted(_hip_runtimes_mapped())))
 
+# every entry point include/pgemm.h declares
+_EXPORTS = ("gemm_f32", "gemm_f64", "matmat_f64", "pgemm_status_string",
+            "pgemm_select_f32", "pgemm_select_f64", "pgemm_variant_name",
+            "pgemm_num_variants", "gemm_f32_variant", "gemm_f64_variant",
+            "gemm_f32_ws", "gemm_f64_ws", "pgemm_workspace_f32", "pgemm_workspace_f64",
+            "matmat_f64_host", "pgemm_matmat_host_workspace", "pgemm_select_ws_f32",
+            "pgemm_select_ws_f64", "pgemm_device_info")
+_missing = [n for n in _EXPORTS if not hasattr(_lib, n)]
+if _missing:
+    raise ImportError("libpgemm.so is older than this binding (no %s); rebuild it with "
+                      "`python precision_gemm_02_amd/build.py`" % ", ".join(_missing))
+
 _i, _f, _d, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 _lib.gemm_f32.argtypes = [_i, _i, _i, _f, _vp, _i, _vp, _i, _f, _vp, _i, _vp]
 _lib.gemm_f64.argtypes = [_i, _i, _i, _d, _vp, _i, _vp, _i, _d, _vp, _i, _vp]
@@ -82,19 +95,16 @@ _lib.pgemm_variant_name.argtypes = [_i]
 _lib.pgemm_variant_name.restype = ctypes.c_char_p
 for _name in ("gemm_f32", "gemm_f64", "matmat_f64", "gemm_f32_variant", "gemm_f64_variant",
               "pgemm_select_f32", "pgemm_select_f64", "pgemm_num_variants", "gemm_f32_ws",
-              "gemm_f64_ws", "pgemm_select_ws_f32", "pgemm_select_ws_f64"):
+              "gemm_f64_ws", "pgemm_select_ws_f32", "pgemm_select_ws_f64",
+              "pgemm_device_info"):
     getattr(_lib, _name).restype = _i
+_lib.pgemm_device_info.argtypes = [ctypes.POINTER(_i), ctypes.POINTER(_i)]
 
 PGEMM_OK = 0
 PGEMM_EHIP = -100
 PGEMM_EVARIANT = -101
 
-EXPORTS = ("gemm_f32", "gemm_f64", "matmat_f64", "pgemm_status_string",
-           "pgemm_select_f32", "pgemm_select_f64", "pgemm_variant_name",
-           "pgemm_num_variants", "gemm_f32_variant", "gemm_f64_variant",
-           "gemm_f32_ws", "gemm_f64_ws", "pgemm_workspace_f32", "pgemm_workspace_f64",
-           "matmat_f64_host", "pgemm_matmat_host_workspace", "pgemm_select_ws_f32",
-           "pgemm_select_ws_f64")
+EXPORTS = _EXPORTS
 
 
 class PgemmError(RuntimeError):
@@ -231,6 +241,13 @@ def select_ws_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws_bytes):
     v = _lib.pgemm_select_ws_f64(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
                                  _addr(C), ldc, ws_bytes, ctypes.byref(sk))
     return v, sk.value
+
+
+def device_info():
+    """(compute units, peak clock in kHz) of the current device."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    _check(_lib.pgemm_device_info(ctypes.byref(cus), ctypes.byref(khz)), "pgemm_device_info")
+    return cus.value, khz.value
 
 
 def variants():

@@ -1,7 +1,9 @@
 """Build libpgemm.so from csrc/ with hipcc for gfx950.
 
 Each .hip file is compiled to an object in parallel, then linked into one
-shared library next to this file.  Usage: ``python -m precision_gemm_02_amd.build``.
+shared library next to this file.  Usage: ``python precision_gemm_02_amd/build.py``
+(run as a file, it does not import the package, whose import needs a
+current library).
 """
 from __future__ import annotations
 

@@ -588,6 +588,17 @@ int pgemm_select_ws_f64(int m, int n, int k, double alpha, const double* A, int 
 
 int pgemm_num_variants(void) { return tables().n32 + tables().n64; }
 
+int pgemm_device_info(int* cus, int* clock_khz) {
+  if (cus == nullptr) return -1;
+  if (clock_khz == nullptr) return -2;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PGEMM_EHIP;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(clock_khz, hipDeviceAttributeClockRate, dev) != hipSuccess)
+    return PGEMM_EHIP;
+  return PGEMM_OK;
+}
+
 const char* pgemm_variant_name(int variant) {
   if (variant >= 1 && variant <= tables().n32) return tables().f32[variant - 1].name;
   const int j = variant - 1 - tables().n32;

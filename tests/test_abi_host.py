@@ -172,6 +172,12 @@ def test_selection_with_workspace():
     assert pg.select_ws_f32(*bad, 1 << 20) == (-6, 0)
 
 
+def test_device_info_argument_codes():
+    out = ctypes.c_int(0)
+    assert L.pgemm_device_info(None, ctypes.byref(out)) == -1
+    assert L.pgemm_device_info(ctypes.byref(out), None) == -2
+
+
 def test_status_strings():
     assert pg.status_string(0) == "success"
     assert "launch" in pg.status_string(pg.PGEMM_EHIP)

@@ -293,6 +293,16 @@ def test_unaligned_pointer_takes_unaligned_path():
     assert_f32_parity(C, oracle_full(p), p.k)
 
 
+def test_device_info():
+    """The device the library runs on, as the HIP runtime reports it: the
+    compute-unit count agrees with torch's, and the peak clock is a plausible
+    one (the MI355X's is 2.4 GHz)."""
+    cus, khz = pg.device_info()
+    assert cus == torch.cuda.get_device_properties(0).multi_processor_count
+    assert 1_000_000 <= khz <= 4_000_000
+    say("device", cus, "CUs at", khz / 1000, "MHz")
+
+
 def test_determinism_bitwise():
     p = gi.workload("sgemm_2048")
     C1, _ = run_colmajor(p)
