@@ -64,13 +64,15 @@ int find_variant(const Variant<T>* table, int count, const char* name) {
   return 0;
 }
 
-// One tile class: the aligned and unaligned variants of one tiling and the
+// One tile class: the aligned and unaligned variants of one tiling, the
 // share of the matrix-core peak its steady state reaches (measured on the
 // MI355X, one round of 256 tiles timed against K: 256x256 154.4, 128x128
-// 153.4, 256x128 152.6 TFLOP/s of 157.3; fp64 128x128 76.9 of 78.6).
+// 153.4, 256x128 152.6 TFLOP/s of 157.3; fp64 128x128 76.9 of 78.6), and
+// any fixed cost per round beyond the common one (seconds).
 struct TileClass {
   int vec, ua;
   double eff;
+  double extra_s;
 };
 
 // Variant tables plus the tile classes the shape/alignment choice uses,
@@ -79,21 +81,21 @@ struct Tables {
   const Variant<float>* f32;
   const Variant<double>* f64;
   int n32, n64;
-  TileClass f32c[4];
+  TileClass f32c[5];
   TileClass f64c[2];
   Tables() {
     f32 = f32_variants(&n32);
     f64 = f64_variants(&n64);
     f32c[0] = {find_variant(f32, n32, "f32_256x256x16_w2x4_s3_vec"),
-               find_variant(f32, n32, "f32_256x256x16_w2x4_s3_ua"), 0.982};
+               find_variant(f32, n32, "f32_256x256x16_w2x4_s3_ua"), 0.982, 0};
     f32c[1] = {find_variant(f32, n32, "f32_256x128x32_w4x2_s3_vec"),
-               find_variant(f32, n32, "f32_256x128x32_w4x2_s3_ua"), 0.970};
+               find_variant(f32, n32, "f32_256x128x32_w4x2_s3_ua"), 0.970, 0};
     // 128 x 128: a ring of 4 stages of BK 16 and 8 waves of 32 x 64; it has
     // the least fixed cost per tile of the 128 x 128 configurations (no
     // hand-over between K groups), which is what decides at these sizes
     // (2048^3 144.5 against 143.2 TFLOP/s for two K groups of 4 waves).
     f32c[2] = {find_variant(f32, n32, "f32_128x128x16_w4x2_s4_vec"),
-               find_variant(f32, n32, "f32_128x128x16_w4x2_s4_ua"), 0.975};
+               find_variant(f32, n32, "f32_128x128x16_w4x2_s4_ua"), 0.975, 0};
     // 64 x 64: small problems, and mid-sized ones whose 128 x 128 tiles
     // would leave a badly filled last round (2500^3 to 3500^3, the ragged
     // 4097 x 3001 x 1023).  Several of these workgroups share a compute unit
@@ -102,7 +104,17 @@ struct Tables {
     // as one round of 256 tiles: 18.9 us (113.8 TFLOP/s) against 32.8 us for
     // 64 tiles of 128 x 128, each with its K loop split over 4 workgroups.
     f32c[3] = {find_variant(f32, n32, "f32_64x64x16_w2x2_s4_vec"),
-               find_variant(f32, n32, "f32_64x64x16_w2x2_s4_ua"), 0.88};
+               find_variant(f32, n32, "f32_64x64x16_w2x2_s4_ua"), 0.88, 0};
+    // 64 x 64 with two K groups of 4 waves (two waves per SIMD): its steady
+    // state keeps ~0.96 of peak where the one-wave-per-SIMD class above
+    // falls to ~0.64 (operands no longer served from the caches: 1024^2 x
+    // 2048 and beyond), and it pays ~1.9 us more per round for the hand-over
+    // of partial sums between the groups.  Fitted to 11 M x N shapes from
+    // 256 x 4096 to 2560^2 at K = 256 ... 8192: the model then picks it from
+    // K ~ 1500 on (measured gains up to 50 % at K >= 2048; at K <= 1024 the
+    // one-group class is up to 12 % faster).
+    f32c[4] = {find_variant(f32, n32, "f32_64x64x32_w2x2_s3_k2_vec"),
+               find_variant(f32, n32, "f32_64x64x32_w2x2_s3_k2_ua"), 0.96, 1.9e-6};
     // fp64: 128 x 128 tiles for large problems.  Their 64 x 32 wave tiles
     // leave registers for the unrolled steady-state loop, which more than
     // pays for the extra operand traffic of smaller tiles (4096^3: 74.0
@@ -111,9 +123,9 @@ struct Tables {
     // 1024^3 60.5 against 17.6 TFLOP/s, 3000^3 70.5 against 53.3; fitted
     // under the round model at ~0.90 of peak.
     f64c[0] = {find_variant(f64, n64, "f64_128x128x16_w2x4_s3_vec"),
-               find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua"), 0.978};
+               find_variant(f64, n64, "f64_128x128x16_w2x4_s3_ua"), 0.978, 0};
     f64c[1] = {find_variant(f64, n64, "f64_64x64x16_w2x4_s4_vec"),
-               find_variant(f64, n64, "f64_64x64x16_w2x4_s4_ua"), 0.90};
+               find_variant(f64, n64, "f64_64x64x16_w2x4_s4_ua"), 0.90, 0};
   }
 };
 
@@ -191,17 +203,19 @@ constexpr double unit_seconds() {
   return 2.0 / ((sizeof(T) == 4 ? 157.3e12 : 78.6e12) / 256);
 }
 
-// A tile's K loop at efficiency eff, and the fixed part of a round: ~1.5 us
-// of prologue and the round's stores of C at ~5 TB/s (both in units).
+// A tile's K loop at the class's efficiency, and the fixed part of a round:
+// ~1.5 us of prologue, the round's stores of C at ~5 TB/s and the class's
+// own extra (all in units).
 template <typename T>
-void round_costs(const Variant<T>& v, double eff, int k, int cus, double* kloop, double* fixed) {
+void round_costs(const Variant<T>& v, const TileClass& tc, int k, int cus, double* kloop,
+                 double* fixed) {
   const double c_bytes = (double)cus * v.bm * v.bn * sizeof(T);
-  *kloop = (double)v.bm * (double)v.bn * (double)k / eff;
-  *fixed = (1.5e-6 + c_bytes / 5e12) / unit_seconds<T>();
+  *kloop = (double)v.bm * (double)v.bn * (double)k / tc.eff;
+  *fixed = (1.5e-6 + tc.extra_s + c_bytes / 5e12) / unit_seconds<T>();
 }
 
 template <typename T>
-SkPlan sk_plan(const Variant<T>& v, double eff, int m, int n, int k, int cus) {
+SkPlan sk_plan(const Variant<T>& v, const TileClass& tc, int m, int n, int k, int cus) {
   SkPlan p;
   const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
@@ -214,7 +228,7 @@ SkPlan sk_plan(const Variant<T>& v, double eff, int m, int n, int k, int cus) {
   if (per_tile > nk / min_iters) per_tile = nk / min_iters;
   const long long s_al = rest * per_tile;
   double kloop, fixed;
-  round_costs(v, eff, k, cus, &kloop, &fixed);
+  round_costs(v, tc, k, cus, &kloop, &fixed);
   long long S = 0;
   double best = 0;
   for (const long long c : {s_al, s_all}) {
@@ -241,12 +255,12 @@ SkPlan sk_plan(const Variant<T>& v, double eff, int m, int n, int k, int cus) {
 // 20 fp32 shapes from 512^3 to 12000 x 2000 x 4000 and 9 fp64 sizes the
 // plain estimate picks the fastest tile class (within 1 %).
 template <typename T>
-double estimate(const Variant<T>& v, double eff, int m, int n, int k, int cus,
+double estimate(const Variant<T>& v, const TileClass& tc, int m, int n, int k, int cus,
                 const SkPlan* sk) {
   const long long tiles = ceil_div(m, v.bm) * ceil_div(n, v.bn);
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
   double kloop, fixed;
-  round_costs(v, eff, k, cus, &kloop, &fixed);
+  round_costs(v, tc, k, cus, &kloop, &fixed);
   const double t = (double)rounds * (kloop + fixed);
   if (rest == 0) return t;
   if (sk != nullptr && sk->wgs > 0)
@@ -270,7 +284,7 @@ Choice choose(int m, int n, int k, bool sk_ok) {
   if constexpr (sizeof(T) == 4) {
     table = t.f32;
     cls = t.f32c;
-    ncls = 4;
+    ncls = 5;
   } else {
     table = t.f64;
     cls = t.f64c;
@@ -282,13 +296,13 @@ Choice choose(int m, int n, int k, bool sk_ok) {
   double best_t = 0;
   for (int c = 0; c < ncls; ++c) {
     const Variant<T>& v = table[cls[c].vec];
-    double e = estimate(v, cls[c].eff, m, n, k, cus, nullptr);
+    double e = estimate(v, cls[c], m, n, k, cus, nullptr);
     bool sk = false;
-    const SkPlan p = (sk_ok && v.sk) ? sk_plan(v, cls[c].eff, m, n, k, cus) : SkPlan{};
+    const SkPlan p = (sk_ok && v.sk) ? sk_plan(v, cls[c], m, n, k, cus) : SkPlan{};
     if (p.wgs > 0) {
       // stream-K only where it is estimated at least 1 % faster: below that
       // the measured gains were within noise or losses
-      const double e_sk = estimate(v, cls[c].eff, m, n, k, cus, &p);
+      const double e_sk = estimate(v, cls[c], m, n, k, cus, &p);
       if (e_sk * 1.01 < e) {
         e = e_sk;
         sk = true;
@@ -321,7 +335,7 @@ int pick(int m, int n, int k, bool vec, size_t ws_bytes, SkPlan* plan) {
   if (ws_bytes > 0) {
     const Choice c = choose<T>(m, n, k, true);
     if (c.sk) {
-      const SkPlan p = sk_plan(table[cls[c.cls].vec], cls[c.cls].eff, m, n, k, device_cus());
+      const SkPlan p = sk_plan(table[cls[c.cls].vec], cls[c.cls], m, n, k, device_cus());
       if (ws_bytes >= p.bytes) {
         *plan = p;
         return vec ? cls[c.cls].vec : cls[c.cls].ua;
@@ -415,9 +429,9 @@ size_t workspace_impl(int m, int n, int k) {
   if (!c.sk) return 0;
   // the aligned and unaligned variants of a tile class share their tiling
   if constexpr (sizeof(T) == 4)
-    return sk_plan(t.f32[t.f32c[c.cls].vec], t.f32c[c.cls].eff, m, n, k, device_cus()).bytes;
+    return sk_plan(t.f32[t.f32c[c.cls].vec], t.f32c[c.cls], m, n, k, device_cus()).bytes;
   else
-    return sk_plan(t.f64[t.f64c[c.cls].vec], t.f64c[c.cls].eff, m, n, k, device_cus()).bytes;
+    return sk_plan(t.f64[t.f64c[c.cls].vec], t.f64c[c.cls], m, n, k, device_cus()).bytes;
 }
 
 template <typename T>

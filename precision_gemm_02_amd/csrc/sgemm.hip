@@ -54,6 +54,11 @@ const Variant<float>* f32_variants(int* count) {
       // workgroups share a compute unit when there are more tiles than units
       PGEMM_F32_SK(64, 64, 16, 2, 2, 4, true, vec),
       PGEMM_F32_SK(64, 64, 16, 2, 2, 4, false, ua),
+      // 64 x 64 tiles with two K groups of 4 waves (8 waves, two per SIMD)
+      // on a ring of 3 stages of BK 32: long K loops on few tiles per
+      // compute unit, where one wave per SIMD cannot hide the memory latency
+      PGEMM_F32_K2(64, 64, 32, 2, 2, 3, true, vec),
+      PGEMM_F32_K2(64, 64, 32, 2, 2, 3, false, ua),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

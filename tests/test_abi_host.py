@@ -127,7 +127,12 @@ def test_selection_by_shape_and_alignment():
     assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_vec")
     # 1024^2: 256 tiles of 64 x 64
     v = pg.select_f32(1024, 1024, 1024, 1.0, FAKE, 1024, FAKE, 1024, 0.0, FAKE, 1024)
-    assert name_of(v).startswith("f32_64x64") and name_of(v).endswith("_vec")
+    assert name_of(v) == "f32_64x64x16_w2x2_s4_vec"
+    # the same tiles with a long K loop: two K groups of 4 waves per tile
+    v = pg.select_f32(1024, 1024, 8192, 1.0, FAKE, 1024, FAKE, 8192, 0.0, FAKE, 1024)
+    assert name_of(v) == "f32_64x64x32_w2x2_s3_k2_vec"
+    v = pg.select_f32(1024, 1024, 8192, 1.0, FAKE_ODD, 1024, FAKE, 8192, 0.0, FAKE, 1024)
+    assert name_of(v) == "f32_64x64x32_w2x2_s3_k2_ua"
     # odd leading dimensions select the unaligned path
     v = pg.select_f32(4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
     assert name_of(v).endswith("_ua")
