@@ -529,18 +529,52 @@ def test_random_shapes_every_entry_exact_integer(case):
         assert_bitwise(run_ws(p), R)
 
 
+# (dtype, m, n, k, (lda, ldb, ldc), the variant the default entry point picks
+# on 256 compute units): one case per tile class and alignment, so that each
+# class the shape choice can return runs through gemm_f32 / gemm_f64 itself.
+CLASS_CASES = [
+    (np.float32, 4096, 4096, 256, (4096, 256, 4096), "f32_256x256x16_w2x4_s3_vec"),
+    (np.float32, 4097, 4095, 255, (4098, 256, 4100), "f32_128x128x16_w4x2_s4_ua"),
+    (np.float32, 2560, 2560, 512, (2560, 512, 2560), "f32_256x128x32_w4x2_s3_vec"),
+    (np.float32, 2561, 2559, 511, (2562, 512, 2564), "f32_256x128x32_w4x2_s3_ua"),
+    (np.float32, 2048, 2048, 1024, (2052, 1028, 2056), "f32_128x128x16_w4x2_s4_vec"),
+    (np.float32, 1000, 700, 900, (1001, 901, 1003), "f32_64x64x16_w2x2_s4_ua"),
+    (np.float32, 1000, 1000, 3000, (1000, 3000, 1000), "f32_64x64x32_w2x2_s3_k2_vec"),
+    (np.float32, 1001, 999, 2500, (1002, 2501, 1004), "f32_64x64x32_w2x2_s3_k2_ua"),
+    (np.float64, 2048, 2048, 512, (2050, 514, 2048), "f64_128x128x16_w2x4_s3_vec"),
+    (np.float64, 2048, 2047, 511, (2049, 512, 2051), "f64_128x128x16_w2x4_s3_ua"),
+    (np.float64, 700, 900, 500, (700, 500, 702), "f64_64x64x16_w2x4_s4_vec"),
+    (np.float64, 701, 899, 501, (702, 501, 703), "f64_64x64x16_w2x4_s4_ua"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CLASS_CASES)), ids=lambda c: CLASS_CASES[c][5])
+def test_every_tile_class_through_the_default_entry_exact_integer(case):
+    dtype, m, n, k, lds, want = CLASS_CASES[case]
+    alpha, beta = ALPHA_BETA[case % len(ALPHA_BETA)]
+    p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=900 + case)
+    dA, dB, dC = DevMat(p.A), DevMat(p.B), DevMat(p.C)
+    sel = pg.select_f32 if dtype == np.float32 else pg.select_f64
+    got = pg.variants()[sel(m, n, k, alpha, dA.ptr, p.lda, dB.ptr, p.ldb, beta, dC.ptr, p.ldc)]
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert got == want, (got, want)
+    say("class", got, (m, n, k), lds, (alpha, beta))
+    C, _ = run_colmajor(p)
+    assert_bitwise(C, oracle_full(p))
+
+
 LONG_CASES = int(os.environ.get("PGEMM_LONG_TESTS", "0"))
 
 
 @pytest.mark.skipif(LONG_CASES <= 0, reason="set PGEMM_LONG_TESTS=<count> to run")
 def test_random_shapes_long():
     """Opt-in long run of the random-shape check (PGEMM_LONG_TESTS=3000 takes
-    about a minute): seeded problems up to 3000 x 3000 x 1500, both
+    about two minutes): seeded problems up to 3000 x 3000 x 3000, both
     precisions, odd or aligned leading dimensions, alpha/beta including
     zero, through gemm_* and gemm_*_ws; bitwise against the oracle."""
     cases = (_random_cases(LONG_CASES * 7 // 10, seed=77)
              + _random_cases(LONG_CASES - LONG_CASES * 7 // 10, seed=78,
-                             mn_range=(1, 3000), k_range=(1, 1500)))
+                             mn_range=(1, 3000), k_range=(1, 3000)))
     for t, (dtype, m, n, k, lds, alpha, beta) in enumerate(cases):
         p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=5000 + t)
         R = oracle_full(p)
