@@ -106,7 +106,7 @@ class Resident:
         # the kernel the entry point launches, and how many stream-K
         # workgroups share the last round (0: none, no fix-up kernel)
         sel = pg.select_ws_f32 if self.dt == "f32" else pg.select_ws_f64
-        vid, self.sk_wgs = sel(*self.args, self.ws_bytes)
+        vid, self.sk_wgs, self.strip_rows = sel(*self.args, self.ws_bytes)
         self.variant = pg.variants().get(vid, "none")
 
     def launch(self):
@@ -250,7 +250,7 @@ def roofline(r: Resident, kern_ms: list):
             "traffic": recorded_traffic(r.variant, r.name),
             "counters": recorded_counters(r.variant, r.name),
             "algorithmic_bytes": r.algorithmic_bytes(),
-            "kernel": r.variant, "stream_k_wgs": r.sk_wgs, "kernel_ms_mean": round(kern_ms_mean, 4),
+            "kernel": r.variant, "stream_k_wgs": r.sk_wgs, "strip_rows": r.strip_rows, "kernel_ms_mean": round(kern_ms_mean, 4),
             "kernel_ms_median": round(float(np.median(kern_ms)), 4),
             "kernel_ms_min": round(float(np.min(kern_ms)), 4),
             "entry": r.entry, "workspace_bytes": r.ws_bytes,

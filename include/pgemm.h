@@ -67,7 +67,9 @@ extern "C" {
  * memory is moved in 16-byte accesses either way (gfx950 needs only dword
  * alignment for them); 16-byte aligned pointers with leading dimensions that
  * are multiples of 4 select kernels that also assume that alignment.  The
- * tile size is chosen per call from the shape.  Leading dimensions so large
+ * tile size is chosen per call from the shape; when only a few rows (at most
+ * 8) lie below the last whole row of tiles, a second kernel may compute them
+ * (both kernels are launched on `stream`).  Leading dimensions so large
  * that one tile's columns span 2 GiB (about ldb >= 2^21 or lda >= 2^24
  * elements) take a slower loading path with 64-bit addresses; the results
  * are the same.
@@ -182,16 +184,19 @@ int pgemm_select_f32(int m, int n, int k, float alpha, const float *A, int lda,
 int pgemm_select_f64(int m, int n, int k, double alpha, const double *A, int lda,
                      const double *B, int ldb, double beta, const double *C, int ldc);
 /* The variant gemm_f32_ws / gemm_f64_ws would launch with a workspace of
- * ws_bytes bytes (0: as without one), same return values as above.  If
- * sk_wgs is not NULL it receives the number of stream-K workgroups that
- * share the last, partly filled round (0: none; then the call launches only
- * the GEMM kernel, otherwise also the fix-up kernel that sums the pieces). */
+ * ws_bytes bytes (0: as without one, i.e. gemm_f32 / gemm_f64), same return
+ * values as above.  If sk_wgs is not NULL it receives the number of
+ * stream-K workgroups that share the last, partly filled round (0: none;
+ * otherwise the call also launches the fix-up kernel that sums the pieces).
+ * If strip_rows is not NULL it receives the number of rows of C below the
+ * last whole tile row that a separate strip kernel computes (0: none; at
+ * most 8; the tiles then cover the first m - strip_rows rows). */
 int pgemm_select_ws_f32(int m, int n, int k, float alpha, const float *A, int lda,
                         const float *B, int ldb, float beta, const float *C, int ldc,
-                        size_t ws_bytes, int *sk_wgs);
+                        size_t ws_bytes, int *sk_wgs, int *strip_rows);
 int pgemm_select_ws_f64(int m, int n, int k, double alpha, const double *A, int lda,
                         const double *B, int ldb, double beta, const double *C, int ldc,
-                        size_t ws_bytes, int *sk_wgs);
+                        size_t ws_bytes, int *sk_wgs, int *strip_rows);
 const char *pgemm_variant_name(int variant);
 int pgemm_num_variants(void);
 /* The current device's compute units and peak clock (kHz), as the HIP

@@ -77,8 +77,10 @@ _lib.gemm_f64_variant.argtypes = [_i] + _lib.gemm_f64.argtypes
 _lib.pgemm_select_f32.argtypes = [_i, _i, _i, _f, _vp, _i, _vp, _i, _f, _vp, _i]
 _lib.pgemm_select_f64.argtypes = [_i, _i, _i, _d, _vp, _i, _vp, _i, _d, _vp, _i]
 _sz = ctypes.c_size_t
-_lib.pgemm_select_ws_f32.argtypes = _lib.pgemm_select_f32.argtypes + [_sz, ctypes.POINTER(_i)]
-_lib.pgemm_select_ws_f64.argtypes = _lib.pgemm_select_f64.argtypes + [_sz, ctypes.POINTER(_i)]
+_lib.pgemm_select_ws_f32.argtypes = _lib.pgemm_select_f32.argtypes + [_sz, ctypes.POINTER(_i),
+                                                                       ctypes.POINTER(_i)]
+_lib.pgemm_select_ws_f64.argtypes = _lib.pgemm_select_f64.argtypes + [_sz, ctypes.POINTER(_i),
+                                                                       ctypes.POINTER(_i)]
 _lib.gemm_f32_ws.argtypes = _lib.gemm_f32.argtypes[:11] + [_vp, _sz, _vp]
 _lib.gemm_f64_ws.argtypes = _lib.gemm_f64.argtypes[:11] + [_vp, _sz, _vp]
 _lib.pgemm_workspace_f32.argtypes = [_i, _i, _i]
@@ -228,19 +230,19 @@ def select_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
 
 
 def select_ws_f32(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws_bytes):
-    """(variant id, stream-K workgroups) gemm_f32_ws would use (0: none)."""
-    sk = ctypes.c_int(0)
+    """(variant id, stream-K workgroups, strip rows) gemm_f32_ws would use."""
+    sk, strip = ctypes.c_int(0), ctypes.c_int(0)
     v = _lib.pgemm_select_ws_f32(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
-                                 _addr(C), ldc, ws_bytes, ctypes.byref(sk))
-    return v, sk.value
+                                 _addr(C), ldc, ws_bytes, ctypes.byref(sk), ctypes.byref(strip))
+    return v, sk.value, strip.value
 
 
 def select_ws_f64(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws_bytes):
-    """(variant id, stream-K workgroups) gemm_f64_ws would use (0: none)."""
-    sk = ctypes.c_int(0)
+    """(variant id, stream-K workgroups, strip rows) gemm_f64_ws would use."""
+    sk, strip = ctypes.c_int(0), ctypes.c_int(0)
     v = _lib.pgemm_select_ws_f64(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
-                                 _addr(C), ldc, ws_bytes, ctypes.byref(sk))
-    return v, sk.value
+                                 _addr(C), ldc, ws_bytes, ctypes.byref(sk), ctypes.byref(strip))
+    return v, sk.value, strip.value
 
 
 def device_info():

@@ -268,13 +268,50 @@ double estimate(const Variant<T>& v, const TileClass& tc, int m, int n, int k, i
   return t + kloop + fixed;
 }
 
-// The tile class with the least estimated time for this shape (with
-// stream-K of the last round where sk_ok and where it is estimated to help).
+// Rows left below the last whole tile row that a separate strip kernel can
+// take (0: none): at most kStripRows of them, and at least one whole tile
+// row above.
+template <typename T>
+int strip_rows(const Variant<T>& v, int m) {
+  const int r = m % v.bm;
+  return (r > 0 && r <= kStripRows && m > v.bm) ? r : 0;
+}
+
+// Estimated time of strip_rows_kernel on r rows (same units as estimate): a
+// launch behind the GEMM kernel (~4 us) plus the largest of: its latency
+// chain (~2.5 us per batch of four steps of every thread, ~2 us for the
+// sums), reading B once from HBM (~4 TB/s), every workgroup's reads of the
+// strip of A from the caches (one 128-byte line per inner index, ~7 TB/s:
+// fitted to 8193 x 8192 x 8192, where they dominate), and its multiply-adds
+// on the vector units (~40 TFLOP/s fp32, ~20 fp64).
+template <typename T>
+double strip_time(int r, int n, int k) {
+  const double s = sizeof(T);
+  const double lat = 2.5e-6 * (double)ceil_div(k, 4 * kStripThreads) + 2e-6;
+  const double b_s = (double)k * n * s / 4e12;
+  const double a_s = (double)ceil_div(n, kStripCols) * (double)k * 128.0 / 7e12;
+  const double f_s = 2.0 * r * (double)n * k / (sizeof(T) == 4 ? 40e12 : 20e12);
+  double t = lat;
+  if (b_s > t) t = b_s;
+  if (a_s > t) t = a_s;
+  if (f_s > t) t = f_s;
+  return (4e-6 + t) / unit_seconds<T>();
+}
+
+// What a call launches: the tile class, its stream-K plan (wgs == 0: none)
+// and the rows left to the strip kernel (0: none).
 struct Choice {
   int cls = 0;
-  bool sk = false;
+  SkPlan plan;
+  int strip = 0;
 };
 
+// The tile class with the least estimated time for this shape, each class
+// weighed with and without the strip kernel for the rows below its last
+// whole tile row (the strip only where it is estimated at least 2 % faster
+// than the class without it), and with stream-K of the last round where
+// sk_ok (only where that is estimated at least 1 % faster: below that the
+// measured gains were within noise or losses).
 template <typename T>
 Choice choose(int m, int n, int k, bool sk_ok) {
   const Tables& t = tables();
@@ -293,56 +330,60 @@ Choice choose(int m, int n, int k, bool sk_ok) {
   const int cus = device_cus();
   if (k <= 0) k = 1;
   Choice best;
-  double best_t = 0;
+  double best_t = -1;
   for (int c = 0; c < ncls; ++c) {
     const Variant<T>& v = table[cls[c].vec];
-    double e = estimate(v, cls[c], m, n, k, cus, nullptr);
-    bool sk = false;
-    const SkPlan p = (sk_ok && v.sk) ? sk_plan(v, cls[c], m, n, k, cus) : SkPlan{};
-    if (p.wgs > 0) {
-      // stream-K only where it is estimated at least 1 % faster: below that
-      // the measured gains were within noise or losses
-      const double e_sk = estimate(v, cls[c], m, n, k, cus, &p);
-      if (e_sk * 1.01 < e) {
-        e = e_sk;
-        sk = true;
+    const int r = strip_rows(v, m);
+    double e_cls = 0;
+    for (int o = 0; o < (r > 0 ? 2 : 1); ++o) {
+      const int strip = o == 0 ? 0 : r;       // rows left to the strip kernel
+      const int mm = m - strip;
+      double e = estimate(v, cls[c], mm, n, k, cus, nullptr);
+      SkPlan plan;
+      const SkPlan p = (sk_ok && v.sk) ? sk_plan(v, cls[c], mm, n, k, cus) : SkPlan{};
+      if (p.wgs > 0) {
+        const double e_sk = estimate(v, cls[c], mm, n, k, cus, &p);
+        if (e_sk * 1.01 < e) {
+          e = e_sk;
+          plan = p;
+        }
       }
-    }
-    if (c == 0 || e < best_t) {
-      best = {c, sk};
-      best_t = e;
+      if (strip > 0) {
+        e += strip_time<T>(strip, n, k);
+        if (e * 1.02 >= e_cls) continue;
+      }
+      e_cls = e;
+      if (best_t < 0 || e < best_t) {
+        best.cls = c;
+        best.plan = plan;
+        best.strip = strip;
+        best_t = e;
+      }
     }
   }
   return best;
 }
 
-// The variant a call launches and its stream-K plan: with a workspace large
-// enough for the plan of the class that is best with stream-K, that class
-// and plan; otherwise the best class without it (and an empty plan).
+// The variant a call launches, its stream-K plan and its strip rows: with a
+// workspace large enough for the plan of the choice that is best with
+// stream-K, that choice; otherwise the best one without stream-K.
 template <typename T>
-int pick(int m, int n, int k, bool vec, size_t ws_bytes, SkPlan* plan) {
+int pick(int m, int n, int k, bool vec, size_t ws_bytes, SkPlan* plan, int* strip) {
   const Tables& t = tables();
-  const Variant<T>* table;
   const TileClass* cls;
-  if constexpr (sizeof(T) == 4) {
-    table = t.f32;
-    cls = t.f32c;
-  } else {
-    table = t.f64;
-    cls = t.f64c;
-  }
-  *plan = SkPlan{};
+  if constexpr (sizeof(T) == 4) cls = t.f32c;
+  else cls = t.f64c;
   if (ws_bytes > 0) {
     const Choice c = choose<T>(m, n, k, true);
-    if (c.sk) {
-      const SkPlan p = sk_plan(table[cls[c.cls].vec], cls[c.cls], m, n, k, device_cus());
-      if (ws_bytes >= p.bytes) {
-        *plan = p;
-        return vec ? cls[c.cls].vec : cls[c.cls].ua;
-      }
+    if (c.plan.wgs == 0 || ws_bytes >= c.plan.bytes) {
+      *plan = c.plan;
+      *strip = c.strip;
+      return vec ? cls[c.cls].vec : cls[c.cls].ua;
     }
   }
   const Choice c = choose<T>(m, n, k, false);
+  *plan = SkPlan{};
+  *strip = c.strip;
   return vec ? cls[c.cls].vec : cls[c.cls].ua;
 }
 
@@ -355,11 +396,12 @@ hipError_t launch_scale(int m, int n, T beta, T* C, int ldc, hipStream_t s) {
                          args, 0, s);
 }
 
-// Launch variant v; with a stream-K plan (decided by pick, whose workspace
-// size pick has checked) the last round's tiles are shared through ws.
+// Launch variant v on the first m - strip rows; with a stream-K plan
+// (decided by pick, whose workspace size pick has checked) the last round's
+// tiles are shared through ws.  The last `strip` rows go to the strip kernel.
 template <typename T>
 int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, const T* B,
-        int ldb, T beta, T* C, int ldc, const SkPlan& plan, T* ws, hipStream_t s) {
+        int ldb, T beta, T* C, int ldc, const SkPlan& plan, T* ws, int strip, hipStream_t s) {
   if (ceil_div(m, v.bm) * ceil_div(n, v.bn) > kMaxTiles) return PGEMM_EHIP;
   GemmArgs<T> g{};
   if (plan.wgs > 0 && ws != nullptr) {
@@ -367,7 +409,7 @@ int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, 
     g.sk_wgs = plan.wgs;
     g.ws = ws;
   }
-  g.M = m;
+  g.M = m - strip;
   g.N = n;
   g.K = k;
   g.alpha = alpha;
@@ -379,7 +421,18 @@ int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, 
   g.ldb = ldb;
   g.ldc = ldc;
   g.group_m = 4;
-  return v.launch(g, s) == hipSuccess ? PGEMM_OK : PGEMM_EHIP;
+  if (v.launch(g, s) != hipSuccess) return PGEMM_EHIP;
+  if (strip > 0) {
+    g.M = m;
+    int i0 = m - strip;
+    void* args[] = {&g, &i0};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&strip_rows_kernel<T>),
+                        dim3((unsigned)ceil_div(n, kStripCols)), dim3(kStripThreads), args, 0,
+                        s) !=
+        hipSuccess)
+      return PGEMM_EHIP;
+  }
+  return PGEMM_OK;
 }
 
 // Shared body of gemm_f32 / gemm_f64 and their forced-variant forms.
@@ -404,7 +457,7 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
     table = tables().f64;
     count = tables().n64;
   }
-  int idx;
+  int idx, strip = 0;
   SkPlan plan;
   if (forced >= 0) {
     if (forced >= count) return PGEMM_EVARIANT;
@@ -414,37 +467,33 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
     // stream-K only where pick chose it: a workspace too small for the
     // preferred plan gives exactly the plain entry point's launch, even if
     // the fallback tiling's own plan would fit
-    idx = pick<T>(m, n, k, vec, ws != nullptr ? ws_bytes : 0, &plan);
+    idx = pick<T>(m, n, k, vec, ws != nullptr ? ws_bytes : 0, &plan, &strip);
   }
   return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, plan,
-             static_cast<T*>(ws), s);
+             static_cast<T*>(ws), strip, s);
 }
 
 // Workspace the stream-K path would use for this shape (0: none).
 template <typename T>
 size_t workspace_impl(int m, int n, int k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
-  const Tables& t = tables();
-  const Choice c = choose<T>(m, n, k, true);
-  if (!c.sk) return 0;
-  // the aligned and unaligned variants of a tile class share their tiling
-  if constexpr (sizeof(T) == 4)
-    return sk_plan(t.f32[t.f32c[c.cls].vec], t.f32c[c.cls], m, n, k, device_cus()).bytes;
-  else
-    return sk_plan(t.f64[t.f64c[c.cls].vec], t.f64c[c.cls], m, n, k, device_cus()).bytes;
+  return choose<T>(m, n, k, true).plan.bytes;
 }
 
 template <typename T>
 int select_impl(int m, int n, int k, T alpha, const T* A, int lda, const T* B, int ldb,
-                const T* C, int ldc, size_t ws_bytes, int* sk_wgs) {
+                const T* C, int ldc, size_t ws_bytes, int* sk_wgs, int* strip_rows_out) {
   if (sk_wgs != nullptr) *sk_wgs = 0;
+  if (strip_rows_out != nullptr) *strip_rows_out = 0;
   const int st = check_args(m, n, k, alpha, A, lda, B, ldb, C, ldc);
   if (st != 0) return st;
   if (m == 0 || n == 0 || k == 0 || alpha == T(0)) return 0;
   const bool vec = vec_ok(A, lda, B, ldb, C, ldc);
   SkPlan plan;
-  const int idx = pick<T>(m, n, k, vec, ws_bytes, &plan);
+  int strip = 0;
+  const int idx = pick<T>(m, n, k, vec, ws_bytes, &plan, &strip);
   if (sk_wgs != nullptr) *sk_wgs = plan.wgs;
+  if (strip_rows_out != nullptr) *strip_rows_out = strip;
   if constexpr (sizeof(T) == 4) return 1 + idx;
   else return 1 + tables().n32 + idx;
 }
@@ -577,27 +626,29 @@ const char* pgemm_status_string(int status) {
 int pgemm_select_f32(int m, int n, int k, float alpha, const float* A, int lda,
                      const float* B, int ldb, float beta, const float* C, int ldc) {
   (void)beta;
-  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc, 0, nullptr);
+  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc, 0, nullptr, nullptr);
 }
 
 int pgemm_select_f64(int m, int n, int k, double alpha, const double* A, int lda,
                      const double* B, int ldb, double beta, const double* C, int ldc) {
   (void)beta;
-  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc, 0, nullptr);
+  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc, 0, nullptr, nullptr);
 }
 
 int pgemm_select_ws_f32(int m, int n, int k, float alpha, const float* A, int lda,
                         const float* B, int ldb, float beta, const float* C, int ldc,
-                        size_t ws_bytes, int* sk_wgs) {
+                        size_t ws_bytes, int* sk_wgs, int* strip_rows) {
   (void)beta;
-  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, sk_wgs);
+  return select_impl<float>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, sk_wgs,
+                            strip_rows);
 }
 
 int pgemm_select_ws_f64(int m, int n, int k, double alpha, const double* A, int lda,
                         const double* B, int ldb, double beta, const double* C, int ldc,
-                        size_t ws_bytes, int* sk_wgs) {
+                        size_t ws_bytes, int* sk_wgs, int* strip_rows) {
   (void)beta;
-  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, sk_wgs);
+  return select_impl<double>(m, n, k, alpha, A, lda, B, ldb, C, ldc, ws_bytes, sk_wgs,
+                             strip_rows);
 }
 
 int pgemm_num_variants(void) { return tables().n32 + tables().n64; }

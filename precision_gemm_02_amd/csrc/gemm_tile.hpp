@@ -1037,6 +1037,78 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs<T> g, int bm, in
   *pc = v;
 }
 
+// Rows of C below the last whole tile row, when there are only a few of
+// them: computing them as tiles would run a full tile's K loop for those
+// rows.  Rows [i0, M) (at most kStripRows), kStripCols consecutive columns
+// per workgroup of kStripThreads threads: thread t sums inner indices t,
+// t + kStripThreads, ... in order (a fused multiply-add per step, the loads
+// of four steps issued together; each value of A, one cache line per inner
+// index, serves all the workgroup's columns), then the partial sums are
+// added by a butterfly of lane exchanges within each wave (which leaves the
+// same total in every lane: each addition pairs the same two values on both
+// lanes) and across the waves in order through LDS.
+constexpr int kStripRows = 8, kStripCols = 8, kStripThreads = 512;
+
+template <typename T>
+__global__ void __launch_bounds__(kStripThreads) strip_rows_kernel(GemmArgs<T> g, int i0) {
+  constexpr int NW = kStripThreads / 64;
+  __shared__ T part[NW][kStripRows][kStripCols];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int j0 = blockIdx.x * kStripCols;
+  const int r = g.M - i0;                      // 1 .. kStripRows
+  const int nc = g.N - j0 < kStripCols ? g.N - j0 : kStripCols;
+  T acc[kStripRows][kStripCols];
+#pragma unroll
+  for (int q = 0; q < kStripRows; ++q)
+#pragma unroll
+    for (int c = 0; c < kStripCols; ++c) acc[q][c] = T(0);
+#pragma unroll 4
+  for (int k = t; k < g.K; k += kStripThreads) {
+    T b[kStripCols];
+#pragma unroll
+    for (int c = 0; c < kStripCols; ++c)
+      b[c] = c < nc ? g.B[(size_t)(j0 + c) * g.ldb + k] : T(0);
+    const T* a = g.A + (size_t)k * g.lda + i0;
+#pragma unroll
+    for (int q = 0; q < kStripRows; ++q) {
+      if (q < r) {
+        const T aq = a[q];
+#pragma unroll
+        for (int c = 0; c < kStripCols; ++c) acc[q][c] = __builtin_fma(aq, b[c], acc[q][c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kStripRows; ++q) {
+    if (q < r) {
+#pragma unroll
+      for (int c = 0; c < kStripCols; ++c) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc[q][c] += __shfl_xor(acc[q][c], off, 64);
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < kStripRows; ++q)
+#pragma unroll
+      for (int c = 0; c < kStripCols; ++c) part[wave][q][c] = acc[q][c];
+  }
+  __syncthreads();
+  if (t < kStripRows * kStripCols) {
+    const int q = t / kStripCols, c = t % kStripCols;
+    if (q < r && c < nc) {
+      T sum = part[0][q][c];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += part[w][q][c];
+      T* pc = g.C + (size_t)(j0 + c) * g.ldc + (i0 + q);
+      T v = g.alpha * sum;
+      if (g.beta != T(0)) v = __builtin_fma(g.beta, *pc, v);
+      *pc = v;
+    }
+  }
+}
+
 // C <- beta*C on the m x n block (the k == 0 / alpha == 0 path); beta == 0
 // writes zeros without reading C.
 template <typename T>

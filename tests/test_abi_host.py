@@ -146,35 +146,43 @@ def test_selection_by_shape_and_alignment():
 
 
 def test_selection_with_workspace():
-    # the ragged 4097 x 3001 x 1023 problem: with the workspace it asks for,
-    # 128 x 128 tiles (3 full rounds of 256 + 24) with 240 stream-K
-    # workgroups (10 per leftover tile: no range crosses a tile); without
-    # it, the plain choice (no stream-K)
-    args = (4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
+    # 2150 x 2030 x 1000: with the workspace it asks for, 128 x 128 tiles (a
+    # full round of 256 + 16) with 240 stream-K workgroups (15 per leftover
+    # tile: no range crosses a tile); without it, or with one byte less, the
+    # plain choice (no stream-K)
+    args = (2150, 2030, 1000, 0.75, FAKE, 2151, FAKE, 1001, -1.25, FAKE, 2153)
     ws = pg.workspace_f32(*args[:3])
-    v, sk = pg.select_ws_f32(*args, ws)
-    assert name_of(v).startswith("f32_128x128") and name_of(v).endswith("_ua") and sk == 240
+    v, sk, strip = pg.select_ws_f32(*args, ws)
+    assert name_of(v) == "f32_128x128x16_w4x2_s4_ua" and sk == 240 and strip == 0
     for short in (0, ws - 1):
-        v0, sk0 = pg.select_ws_f32(*args, short)
-        assert v0 == pg.select_f32(*args) and sk0 == 0
+        v0, sk0, strip0 = pg.select_ws_f32(*args, short)
+        assert v0 == pg.select_f32(*args) and sk0 == 0 and strip0 == 0
+    # the ragged 4097 x 3001 x 1023 problem: row 4097 goes to the strip
+    # kernel and 128 x 128 tiles fill 3 rounds exactly, with or without a
+    # workspace (it asks for none)
+    args = (4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
+    assert pg.workspace_f32(*args[:3]) == 0
+    v, sk, strip = pg.select_ws_f32(*args, 0)
+    assert name_of(v) == "f32_128x128x16_w4x2_s4_ua" and sk == 0 and strip == 1
+    assert v == pg.select_f32(*args)
     # shapes that fill whole rounds: same as the plain entry point
     sq = (8192, 8192, 8192, 1.5, FAKE, 8192, FAKE, 8192, 0.5, FAKE, 8192)
-    assert pg.select_ws_f32(*sq, 1 << 30) == (pg.select_f32(*sq), 0)
+    assert pg.select_ws_f32(*sq, 1 << 30) == (pg.select_f32(*sq), 0, 0)
     d = (4096, 4096, 4096, 1.0, FAKE, 4104, FAKE, 4104, 1.0, FAKE, 4104)
-    assert pg.select_ws_f64(*d, 1 << 30) == (pg.select_f64(*d), 0)
+    assert pg.select_ws_f64(*d, 1 << 30) == (pg.select_f64(*d), 0, 0)
     # 8 leftover 128 x 128 tiles of 50 K tiles: 12 workgroups per tile (each
     # keeps at least 4 K tiles) -> 96, no range crossing a tile
     e = (725, 5528, 796, 1.0, FAKE, 725, FAKE, 796, 1.0, FAKE, 725)
-    v, sk = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
+    v, sk, _ = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
     assert name_of(v).startswith("f32_128x128") and sk == 96
     # 136 leftover tiles (above half the units): all 256 units, ranges of
     # 32-33 K tiles that cross tiles
     e = (1743, 3551, 988, 1.0, FAKE, 1743, FAKE, 988, 1.0, FAKE, 1743)
-    v, sk = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
+    v, sk, _ = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
     assert name_of(v).startswith("f32_128x128") and sk == 256
     # invalid arguments: the same status as the plain selector, no stream-K
     bad = (4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4)
-    assert pg.select_ws_f32(*bad, 1 << 20) == (-6, 0)
+    assert pg.select_ws_f32(*bad, 1 << 20) == (-6, 0, 0)
 
 
 def test_device_info_argument_codes():
@@ -213,11 +221,14 @@ def test_workspace_sizes():
     assert pg.workspace_f32(8192, 8192, 8192) == 0
     assert pg.workspace_f32(2048, 2048, 2048) == 0
     assert pg.workspace_f32(0, 10, 10) == 0 and pg.workspace_f32(10, 10, 0) == 0
-    # 4097 x 3001 x 1023 on 128 x 128 x 16 tiles: 33 x 24 = 792 tiles = 3
-    # rounds of 256 + 24 leftover tiles (64 K tiles each) shared by 240
+    # 2150 x 2030 x 1000 on 128 x 128 x 16 tiles: 17 x 16 = 272 tiles = a
+    # round of 256 + 16 leftover tiles (63 K tiles each) shared by 240
     # workgroups, two workspace slots each.  256 compute units: the MI355X,
     # and the fallback with no GPU.
-    assert pg.workspace_f32(4097, 3001, 1023) == 2 * 240 * 128 * 128 * 4
+    assert pg.workspace_f32(2150, 2030, 1000) == 2 * 240 * 128 * 128 * 4
+    # 4097 x 3001 x 1023: the strip kernel takes the last row, and the tiles
+    # of the other 4096 fill 3 rounds: no workspace
+    assert pg.workspace_f32(4097, 3001, 1023) == 0
     # 3840^3: 900 tiles of 128^2 = 3 rounds + 132, a last round above half
     # full, still shared
     assert pg.workspace_f32(3840, 3840, 3840) == 2 * 256 * 128 * 128 * 4

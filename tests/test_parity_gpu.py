@@ -317,7 +317,7 @@ def test_concurrent_calls_on_two_streams():
     the same call gives alone: the library keeps no per-call state and its
     launches are ordered only by their own stream."""
     import threading
-    p32 = exact_problem(np.float32, 2053, 2048, 1000, 1.5, 0.5, (2055, 1001, 2057), seed=700)
+    p32 = exact_problem(np.float32, 2150, 2030, 1000, 1.5, 0.5, (2151, 1001, 2153), seed=700)
     p64 = exact_problem(np.float64, 900, 1100, 500, 0.75, -1.25, (901, 500, 902), seed=701)
     ref32 = oracle_full(p32)
     ref64 = oracle_full(p64)
@@ -451,7 +451,7 @@ def run_ws(p, ws_bytes=None):
 # ragged M/N edges and K tails inside the shared tiles, and up to 42 pieces
 # summed per tile.
 SK_SHAPES = [
-    (np.float32, 2053, 2048, 1000),    # 128^2: 256 + 16, S 240 aligned, K tail 8
+    (np.float32, 2150, 2030, 1000),    # 128^2: 256 + 16, S 240 aligned, K tail 8
     (np.float32, 725, 5528, 796),      # 128^2: 256 + 8, S 96 aligned, K tail 12
     (np.float32, 1134, 4856, 1042),    # 128^2: 256 + 86, I 22-23, crossing, K tail 2
     (np.float32, 1743, 3551, 988),     # 128^2: 256 + 136, I 32-33, crossing, K tail 12
@@ -534,7 +534,8 @@ def test_random_shapes_every_entry_exact_integer(case):
 # class the shape choice can return runs through gemm_f32 / gemm_f64 itself.
 CLASS_CASES = [
     (np.float32, 4096, 4096, 256, (4096, 256, 4096), "f32_256x256x16_w2x4_s3_vec"),
-    (np.float32, 4097, 4095, 255, (4098, 256, 4100), "f32_128x128x16_w4x2_s4_ua"),
+    (np.float32, 4097, 4095, 255, (4098, 256, 4100), "f32_256x256x16_w2x4_s3_ua"),
+    (np.float32, 2047, 2047, 1023, (2048, 1024, 2050), "f32_128x128x16_w4x2_s4_ua"),
     (np.float32, 2560, 2560, 512, (2560, 512, 2560), "f32_256x128x32_w4x2_s3_vec"),
     (np.float32, 2561, 2559, 511, (2562, 512, 2564), "f32_256x128x32_w4x2_s3_ua"),
     (np.float32, 2048, 2048, 1024, (2052, 1028, 2056), "f32_128x128x16_w4x2_s4_vec"),
@@ -563,6 +564,53 @@ def test_every_tile_class_through_the_default_entry_exact_integer(case):
     assert_bitwise(C, oracle_full(p))
 
 
+# (dtype, m, n, k, (lda, ldb, ldc), workspace?, strip rows, stream-K?): a few
+# rows below the last whole tile row go to the strip kernel (rows as the
+# library chooses them on 256 compute units).  Every tile class under it,
+# both alignments, K below the thread count (most threads without an inner
+# index), column counts that leave the last workgroup 1 to 7 columns, and
+# the strip beside a stream-K launch.
+STRIP_CASES = [
+    (np.float32, 4097, 3001, 1023, (4098, 1024, 4100), False, 1, False),   # 128^2
+    (np.float32, 4100, 4096, 2048, (4100, 2048, 4100), False, 4, False),   # 256^2, vec
+    (np.float32, 2051, 2047, 1999, (2052, 2000, 2054), False, 3, False),   # K tail
+    (np.float32, 3332, 4965, 16, (3333, 17, 3335), False, 4, False),       # 256x128, K 16
+    (np.float32, 1158, 894, 442, (1159, 443, 1161), False, 6, False),      # 64^2
+    (np.float32, 1029, 1024, 3000, (1030, 3001, 1032), False, 5, False),   # 64^2, 2 K groups
+    (np.float64, 900, 4726, 966, (901, 967, 903), True, 4, True),          # with stream-K
+    (np.float64, 2055, 2047, 1501, (2056, 1502, 2058), False, 7, False),   # fp64 128^2, vec
+    (np.float64, 773, 5207, 25, (774, 26, 775), False, 5, False),          # fp64 128^2, K 25
+    (np.float64, 1798, 551, 192, (1799, 193, 1801), False, 6, False),      # fp64 64^2
+]
+
+
+@pytest.mark.parametrize("case", range(len(STRIP_CASES)))
+def test_strip_rows_exact_integer(case):
+    dtype, m, n, k, lds, use_ws, rows, sk = STRIP_CASES[case]
+    alpha, beta = ALPHA_BETA[case % len(ALPHA_BETA)]
+    p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=950 + case)
+    sel = pg.select_ws_f32 if dtype == np.float32 else pg.select_ws_f64
+    dA, dB, dC = DevMat(p.A), DevMat(p.B), DevMat(p.C)
+    v, sk_wgs, strip = sel(m, n, k, alpha, dA.ptr, p.lda, dB.ptr, p.ldb, beta, dC.ptr, p.ldc,
+                           ws_size(p) if use_ws else 0)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert strip == rows and (sk_wgs > 0) == sk, (strip, sk_wgs)
+    say("strip", pg.variants()[v], (m, n, k), lds, (alpha, beta), "rows", strip, "sk", sk_wgs)
+    R = oracle_full(p)
+    C = run_ws(p) if use_ws else run_colmajor(p)[0]
+    assert_bitwise(C, R)
+
+
+def test_strip_rows_beta_zero_ignores_nan_in_c():
+    """beta == 0: the strip rows, like the tiles, never read C."""
+    p = exact_problem(np.float32, 4097, 3001, 1023, 1.0, 0.0, (4098, 1024, 4100), seed=970)
+    R = oracle_full(p)            # C is zero here; with beta == 0 it does not matter
+    p.C = np.full_like(p.C, np.nan)
+    C, _ = run_colmajor(p)
+    assert not np.isnan(C).any()
+    assert_bitwise(C, R)
+
+
 LONG_CASES = int(os.environ.get("PGEMM_LONG_TESTS", "0"))
 
 
@@ -586,14 +634,22 @@ def test_random_shapes_long():
             say("long random", t, np.dtype(dtype).name, (m, n, k), lds, (alpha, beta))
 
 
-def test_stream_k_ragged_workload_parity():
+def test_ragged_workload_strip_parity():
+    """The ragged 4097 x 3001 x 1023 workload: 128 x 128 tiles on the first
+    4096 rows (3 whole rounds) and the strip kernel on the last row, through
+    both entry points (the workspace one asks for no workspace here)."""
     p = gi.workload("sgemm_ragged")
-    assert ws_size(p) > 0
-    C = run_ws(p)
+    dA, dB, dC = DevMat(p.A), DevMat(p.B), DevMat(p.C)
+    v, sk, strip = pg.select_ws_f32(p.m, p.n, p.k, p.alpha, dA.ptr, p.lda, dB.ptr, p.ldb,
+                                    p.beta, dC.ptr, p.ldc, ws_size(p))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert strip == 1 and sk == 0 and ws_size(p) == 0
+    C, _ = run_colmajor(p)
     maxabs, rel = assert_f32_parity(C, oracle_full(p), p.k)
-    say("ragged stream-K max|dC| %.3g rel %.3g" % (maxabs, rel))
+    say("ragged", pg.variants()[v], "strip", strip, "max|dC| %.3g rel %.3g" % (maxabs, rel))
+    assert np.array_equal(run_ws(p).view(np.uint32), C.view(np.uint32))
     q = gi.workload("sgemm_ragged", dist_override="i2")
-    assert_bitwise(run_ws(q), oracle_full(q))
+    assert_bitwise(run_colmajor(q)[0], oracle_full(q))
 
 
 def test_stream_k_fp64_parity():
@@ -604,7 +660,7 @@ def test_stream_k_fp64_parity():
 
 
 def test_stream_k_deterministic_and_small_workspace_is_plain():
-    p = gi.make_colmajor_problem("skdet", np.float32, 2053, 2048, 1000, 2053, 1000, 2053,
+    p = gi.make_colmajor_problem("skdet", np.float32, 2150, 2030, 1000, 2150, 1000, 2150,
                                  1.5, 0.5, seed=32, dist="u", c_dist="u")
     need = ws_size(p)
     C1, C2 = run_ws(p), run_ws(p)
