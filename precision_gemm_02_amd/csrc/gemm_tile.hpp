@@ -312,8 +312,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   // stream-K workgroups (blockIdx >= full_tiles) share the K tiles of the
   // remaining tiles evenly: workgroup w takes iterations [w*I/P, (w+1)*I/P)
   // of the I = rest*nk iterations in (tile, K tile) order, which is the end
-  // of one tile and the start of the next at most (P >= rest); piece j of
-  // workgroup w writes its raw partial sums to workspace slot 2w + j.
+  // of one tile and the start of the next at most (P > rest, so a range is
+  // shorter than a tile); piece j of workgroup w writes its raw partial sums
+  // to workspace slot 2w + j.
   const int nk_all = (g.K + BK - 1) / BK;
   const bool sk_wg = SKP && (int)blockIdx.x >= g.full_tiles;
   const int w_sk = (int)blockIdx.x - g.full_tiles;
