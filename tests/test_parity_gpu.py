@@ -443,31 +443,31 @@ def run_ws(p, ws_bytes=None):
 # (dtype, m, n, k): each leaves a partly filled last round of tiles on 256
 # compute units and so takes the stream-K path (tiling and plan as the
 # library chooses them on 256 units: R full rounds + the rest, S stream-K
-# workgroups of I iterations; "aligned": S is a multiple of the shared tiles
-# and no range crosses a tile; "crossing": some workgroups run two pieces).
+# workgroups; "aligned": no range crosses a tile; "crossing": some
+# workgroups run two pieces).
 # Together they cover every tile class with a stream-K form in both
 # precisions, last rounds below and above half full and no full round at
 # all, aligned and crossing plans, fewer workgroups than compute units,
-# ragged M/N edges and K tails inside the shared tiles, and up to 42 pieces
+# ragged M/N edges and K tails inside the shared tiles, and up to 25 pieces
 # summed per tile.
 SK_SHAPES = [
     (np.float32, 2150, 2030, 1000),    # 128^2: 256 + 16, S 240 aligned, K tail 8
-    (np.float32, 725, 5528, 796),      # 128^2: 256 + 8, S 96 aligned, K tail 12
-    (np.float32, 1134, 4856, 1042),    # 128^2: 256 + 86, I 22-23, crossing, K tail 2
-    (np.float32, 1743, 3551, 988),     # 128^2: 256 + 136, I 32-33, crossing, K tail 12
-    (np.float64, 2812, 2428, 1238),    # fp64 128^2: 256 + 162, crossing, K tail 6
-    (np.float64, 3789, 3267, 211),     # fp64 128^2: 3*256 + 12, S 36 aligned, K tail 3
-    (np.float64, 2398, 2258, 1304),    # fp64 128^2: 256 + 86, crossing, K tail 8
-    (np.float32, 4121, 344, 2015),     # 64^2: 256 + 134, I 65-66, crossing, K tail 15
-    (np.float64, 264, 4934, 1341),     # fp64 64^2: 256 + 134, crossing, K tail 13
-    (np.float64, 284, 3284, 656),      # fp64 64^2: 256 + 4, S 40 aligned
+    (np.float32, 3695, 1115, 669),     # 128^2: 256 + 5, S 50 aligned, K tail 13
+    (np.float32, 2369, 2254, 1108),    # 128^2: 256 + 86, crossing, K tail 4
+    (np.float32, 1351, 4463, 1130),    # 128^2: 256 + 129 (above half), crossing
+    (np.float64, 1988, 4739, 1071),    # fp64 128^2: 2*256 + 96, crossing, K tail 15
+    (np.float64, 6764, 981, 1771),     # fp64 128^2: 256 + 168, crossing, K tail 11
+    (np.float64, 1147, 3951, 809),     # fp64 128^2: 256 + 23, S 253 aligned, K tail 9
+    (np.float32, 2414, 530, 1338),     # 64^2: 256 + 86, crossing, K tail 10
+    (np.float32, 198, 6190, 2096),     # 64^2: 256 + 132, crossing
+    (np.float64, 200, 5553, 967),      # fp64 64^2: 256 + 92, crossing, K tail 7
+    (np.float64, 9224, 73, 539),       # fp64 64^2: 256 + 34, S 238 aligned, K tail 11
     # no full round: every tile shared (at least 2 K tiles per workgroup)
-    (np.float32, 68, 2807, 1579),      # 88 edge tiles of 64^2, I 34-35, crossing
-    (np.float64, 3009, 87, 1029),      # 96 fp64 edge tiles, crossing, K tail 5
-    (np.float32, 255, 140, 819),       # 12 edge tiles, S 252 aligned, K tail 3
-    (np.float32, 70, 163, 913),        # 6 edge tiles, S 174, 29 pieces each, K tail 1
-    (np.float32, 130, 70, 2000),       # 6 edge tiles, 42 pieces each, I 2-3
-    (np.float64, 74, 104, 771),        # 4 fp64 edge tiles, S 96 aligned, K tail 3
+    (np.float32, 67, 4253, 2126),      # 134 edge tiles of 64^2, crossing, K tail 14
+    (np.float32, 66, 93, 794),         # 4 edge tiles, S 100, 25 pieces each, K tail 10
+    (np.float32, 2885, 68, 1923),      # 92 edge tiles, crossing, K tail 3
+    (np.float64, 65, 2145, 1849),      # 68 fp64 edge tiles, crossing, K tail 9
+    (np.float64, 136, 83, 606),        # 6 fp64 edge tiles, S 114, 19 pieces each
 ]
 
 
@@ -572,15 +572,15 @@ def test_every_tile_class_through_the_default_entry_exact_integer(case):
 # the strip beside a stream-K launch.
 STRIP_CASES = [
     (np.float32, 4097, 3001, 1023, (4098, 1024, 4100), False, 1, False),   # 128^2
-    (np.float32, 4100, 4096, 2048, (4100, 2048, 4100), False, 4, False),   # 256^2, vec
     (np.float32, 2051, 2047, 1999, (2052, 2000, 2054), False, 3, False),   # K tail
-    (np.float32, 3332, 4965, 16, (3333, 17, 3335), False, 4, False),       # 256x128, K 16
-    (np.float32, 1158, 894, 442, (1159, 443, 1161), False, 6, False),      # 64^2
-    (np.float32, 1029, 1024, 3000, (1030, 3001, 1032), False, 5, False),   # 64^2, 2 K groups
-    (np.float64, 900, 4726, 966, (901, 967, 903), True, 4, True),          # with stream-K
-    (np.float64, 2055, 2047, 1501, (2056, 1502, 2058), False, 7, False),   # fp64 128^2, vec
-    (np.float64, 773, 5207, 25, (774, 26, 775), False, 5, False),          # fp64 128^2, K 25
-    (np.float64, 1798, 551, 192, (1799, 193, 1801), False, 6, False),      # fp64 64^2
+    (np.float32, 4357, 3791, 16, (4360, 16, 4360), False, 5, False),       # 256^2, vec, K 16
+    (np.float32, 3589, 2302, 36, (3590, 37, 3592), False, 5, False),       # 256x128, K 36
+    (np.float32, 8199, 74, 655, (8200, 656, 8202), False, 7, False),       # 64^2
+    (np.float32, 391, 2418, 1564, (392, 1565, 394), False, 7, False),      # 64^2, 2 K groups
+    (np.float64, 1797, 4713, 737, (1798, 738, 1799), True, 5, True),       # with stream-K
+    (np.float64, 771, 5098, 168, (772, 168, 772), False, 3, False),        # fp64 128^2, vec
+    (np.float64, 1921, 2120, 24, (1922, 25, 1923), False, 1, False),       # fp64 128^2, K 24
+    (np.float64, 134, 5997, 230, (135, 231, 137), False, 6, False),        # fp64 64^2
 ]
 
 
@@ -653,7 +653,7 @@ def test_ragged_workload_strip_parity():
 
 
 def test_stream_k_fp64_parity():
-    p = gi.make_colmajor_problem("sk64", np.float64, 2812, 2428, 1238, 2813, 1238, 2815,
+    p = gi.make_colmajor_problem("sk64", np.float64, 1988, 4739, 1071, 1989, 1071, 1991,
                                  0.75, -1.25, seed=31, dist="n", c_dist="n")
     assert ws_size(p) > 0
     assert_f64_parity(run_ws(p), oracle_full(p))
