@@ -254,9 +254,10 @@ SkPlan sk_plan(const Variant<T>& v, const TileClass& tc, int m, int n, int k, in
 // (every compute unit busy with one tile) costs the tile's K loop at the
 // class's efficiency plus the fixed part (round_costs).  The last, partly
 // filled round costs a whole round, or with a stream-K plan (`sk`) its
-// sk_time.  Edge tiles cost as much as inner ones (they run the same loop).  On
-// 20 fp32 shapes from 512^3 to 12000 x 2000 x 4000 and 9 fp64 sizes the
-// plain estimate picks the fastest tile class (within 1 %).
+// sk_time.  Edge tiles cost as much as inner ones (they run the same loop).
+// Against every class timed on 70 random shapes not used in the fit, the
+// choice runs on average within 1.1 % of the fastest one (7 shapes lose more
+// than 3 %, at most 10 %).
 template <typename T>
 double estimate(const Variant<T>& v, const TileClass& tc, int m, int n, int k, int cus,
                 const SkPlan* sk) {
