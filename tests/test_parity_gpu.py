@@ -455,9 +455,8 @@ SK_SHAPES = [
     (np.float32, 3695, 1115, 669),     # 128^2: 256 + 5, S 50 aligned, K tail 13
     (np.float32, 2369, 2254, 1108),    # 128^2: 256 + 86, crossing, K tail 4
     (np.float32, 1351, 4463, 1130),    # 128^2: 256 + 129 (above half), crossing
-    (np.float64, 1988, 4739, 1071),    # fp64 128^2: 2*256 + 96, crossing, K tail 15
-    (np.float64, 6764, 981, 1771),     # fp64 128^2: 256 + 168, crossing, K tail 11
-    (np.float64, 1147, 3951, 809),     # fp64 128^2: 256 + 23, S 253 aligned, K tail 9
+    (np.float64, 1348, 3029, 2466),    # fp64 128^2: 256 + 8, 32 aligned pieces a tile
+    (np.float64, 3196, 5224, 385),     # fp64 128^2: 4*256 + 1, S 6, K tail 1
     (np.float32, 2414, 530, 1338),     # 64^2: 256 + 86, crossing, K tail 10
     (np.float32, 198, 6190, 2096),     # 64^2: 256 + 132, crossing
     (np.float64, 200, 5553, 967),      # fp64 64^2: 256 + 92, crossing, K tail 7
@@ -569,7 +568,7 @@ def test_every_tile_class_through_the_default_entry_exact_integer(case):
 # library chooses them on 256 compute units).  Every tile class under it,
 # both alignments, K below the thread count (most threads without an inner
 # index), column counts that leave the last workgroup 1 to 7 columns, and
-# the strip beside a stream-K launch.
+# the workspace entry point (which asks for no workspace for these shapes).
 STRIP_CASES = [
     (np.float32, 4097, 3001, 1023, (4098, 1024, 4100), False, 1, False),   # 128^2
     (np.float32, 2051, 2047, 1999, (2052, 2000, 2054), False, 3, False),   # K tail
@@ -577,9 +576,9 @@ STRIP_CASES = [
     (np.float32, 3589, 2302, 36, (3590, 37, 3592), False, 5, False),       # 256x128, K 36
     (np.float32, 8199, 74, 655, (8200, 656, 8202), False, 7, False),       # 64^2
     (np.float32, 391, 2418, 1564, (392, 1565, 394), False, 7, False),      # 64^2, 2 K groups
-    (np.float64, 1797, 4713, 737, (1798, 738, 1799), True, 5, True),       # with stream-K
-    (np.float64, 771, 5098, 168, (772, 168, 772), False, 3, False),        # fp64 128^2, vec
-    (np.float64, 1921, 2120, 24, (1922, 25, 1923), False, 1, False),       # fp64 128^2, K 24
+    (np.float64, 2053, 4032, 157, (2054, 158, 2055), True, 5, False),      # workspace entry
+    (np.float64, 1796, 2244, 142, (1796, 142, 1796), False, 4, False),     # fp64 128^2, vec
+    (np.float64, 1926, 6455, 21, (1927, 22, 1928), False, 6, False),       # fp64 128^2, K 21
     (np.float64, 134, 5997, 230, (135, 231, 137), False, 6, False),        # fp64 64^2
 ]
 
@@ -653,7 +652,7 @@ def test_ragged_workload_strip_parity():
 
 
 def test_stream_k_fp64_parity():
-    p = gi.make_colmajor_problem("sk64", np.float64, 1988, 4739, 1071, 1989, 1071, 1991,
+    p = gi.make_colmajor_problem("sk64", np.float64, 200, 5553, 967, 201, 967, 203,
                                  0.75, -1.25, seed=31, dist="n", c_dist="n")
     assert ws_size(p) > 0
     assert_f64_parity(run_ws(p), oracle_full(p))
