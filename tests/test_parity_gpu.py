@@ -130,8 +130,11 @@ def test_workload_dgemm_rowmajor_sampled_and_freivalds():
     assert err <= 1e-12
 
 
+# the last two: N3 (the swapped problem's m) a few rows past whole 128-row
+# tiles, so the strip kernel takes them (4 and 7 rows on 256 compute units)
 @pytest.mark.parametrize("N1,N2,N3,pad", [(1, 1, 1, 0), (37, 53, 29, 8), (300, 257, 129, 2),
-                                          (512, 512, 512, 8)])
+                                          (512, 512, 512, 8), (2244, 142, 1796, 0),
+                                          (2047, 1501, 2055, 1)])
 def test_matmat_f64_full_oracle(N1, N2, N3, pad):
     p = gi.make_rowmajor_problem("mm", N1, N2, N3, N2 + pad, N3 + pad, N3 + pad, 1.0, 1.0,
                                  seed=N1 + N2)
