@@ -330,626 +330,626 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   }
   auto tile_piece = [&](const int t_lin, const int kt_begin, const int kt_end,
                         const int slot) __attribute__((always_inline)) {
-  int tm, tn;
-  raster(t_lin, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // KS groups of WGM x WGN waves; every group covers the whole tile and takes
-  // 1/KS of the inner-index groups of each K tile.
-  const int kgrp = (KS == 1) ? 0 : wave / (WGM * WGN);
-  const int wave_in = (KS == 1) ? wave : wave % (WGM * WGN);
-  const int wrow = (wave_in % WGM) * Cfg::WM, wcol = (wave_in / WGM) * Cfg::WN;
-  const int M = g.M, N = g.N, K = g.K;
-  const int lda = g.lda, ldb = g.ldb;
-  const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
+    int tm, tn;
+    raster(t_lin, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // KS groups of WGM x WGN waves; every group covers the whole tile and takes
+    // 1/KS of the inner-index groups of each K tile.
+    const int kgrp = (KS == 1) ? 0 : wave / (WGM * WGN);
+    const int wave_in = (KS == 1) ? wave : wave % (WGM * WGN);
+    const int wrow = (wave_in % WGM) * Cfg::WM, wcol = (wave_in / WGM) * Cfg::WN;
+    const int M = g.M, N = g.N, K = g.K;
+    const int lda = g.lda, ldb = g.ldb;
+    const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
 
-  // Per-thread load assignment.  Chunk q = tid + i*NT.
-  //  A: column q / (BM/V), rows (q % (BM/V))*V .. +V-1 of the tile.
-  //  B: column q / KC, inner indices (q % KC)*V .. +V-1 of the tile.
-  chunk_t ra[A_LOADS], rb[B_LOADS];
+    // Per-thread load assignment.  Chunk q = tid + i*NT.
+    //  A: column q / (BM/V), rows (q % (BM/V))*V .. +V-1 of the tile.
+    //  B: column q / KC, inner indices (q % KC)*V .. +V-1 of the tile.
+    chunk_t ra[A_LOADS], rb[B_LOADS];
 
-  // Whole K tiles: unmasked buffer loads, no branches.  A thread's chunks
-  // i = 0, 1, ... of a tile lie NT/(BM/V) columns of A apart, so A needs one
-  // per-lane offset and a scalar step per chunk; each B chunk keeps its own
-  // per-lane offset.  The descriptors move by whole K tiles (scalar work).
-  // Tiles on the M or N edge take the same loads.  An A chunk whose rows
-  // all lie at or beyond M, or a B column at or beyond N, only feeds entries
-  // of C that are never stored, so it is read from the tile's first row /
-  // column instead (in bounds; the values do not matter).  An A chunk that
-  // straddles M (M not a multiple of V) is read whole: its elements past row
-  // M-1 are the column's padding or, with a tight lda, the first V-2 rows of
-  // the next column, and again only feed rows that are never stored.  Such
-  // reads stay inside the (K-1)*lda + M elements of A when the column is not
-  // the last one and lda >= V-1, so on the M edge the steady state stops
-  // before the last column (k_whole) and the masked loads take the rest.
-  static_assert(NT % (BM / V) == 0 && NT % KC == 0, "uniform steps between a thread's chunks");
-  // Byte offsets from the tile's first row (A, in the tile's K tile) and
-  // first column (B): A chunk i of tile kt is at a_off + i*a_step from
-  // A + m0 + kt*BK*lda, B chunk i at b_off[i] from B + n0*ldb + kt*BK.
-  // (Formed in 64 bits; they fit 32 when g.buf32 is set, and are unused
-  // otherwise.)
-  const int a_row = m0 + (tid % (BM / V)) * V;
-  constexpr long long TS = sizeof(T);
-  const int a_off =
-      (int)(((long long)(tid / (BM / V)) * lda + (a_row < M ? a_row - m0 : 0)) * TS);
-  constexpr int A_COLS = NT / (BM / V);   // columns of A between a thread's chunks
-  const int a_step = (int)((long long)A_COLS * lda * TS);
-  int b_off[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int nn = tid / KC + i * (NT / KC);
-    b_off[i] = (int)(((long long)(n0 + nn < N ? nn : 0) * ldb + (tid % KC) * V) * TS);
-  }
-  const T* const a_tile = g.A + m0;
-  const T* const b_tile = g.B + (size_t)n0 * ldb;
-  const bool straddle = (m0 + BM > M) && (M % V != 0);
-  const bool edge_fast = !straddle || lda >= V - 1;
-  const int k_whole = straddle ? (K - 1) / BK : K / BK;   // whole K tiles the loop may load
-  auto gload_full = [&](int kt) {
-    const __amdgpu_buffer_rsrc_t ar = tile_rsrc(a_tile + (size_t)kt * BK * (size_t)lda);
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) ra[i] = load_chunk_buf<TR>(ar, a_off, i * a_step);
-    const __amdgpu_buffer_rsrc_t br = tile_rsrc(b_tile + (size_t)kt * BK);
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) rb[i] = load_chunk_buf<TR>(br, b_off[i], 0);
-  };
-  // Edge tiles and the K tail: out-of-range elements load as zero.
-  auto gload_masked = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int q = tid + i * NT;
-      const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
-      const int k = k0 + kk, m = m0 + mm;
-      const int valid = (k < K) ? min(M - m, V) : 0;
-      if (valid > 0) ra[i] = load_chunk<TR, VEC>(g.A + (size_t)k * lda + m, valid);
-      else ra[i] = chunk_t{};
-    }
-#pragma unroll
+    // Whole K tiles: unmasked buffer loads, no branches.  A thread's chunks
+    // i = 0, 1, ... of a tile lie NT/(BM/V) columns of A apart, so A needs one
+    // per-lane offset and a scalar step per chunk; each B chunk keeps its own
+    // per-lane offset.  The descriptors move by whole K tiles (scalar work).
+    // Tiles on the M or N edge take the same loads.  An A chunk whose rows
+    // all lie at or beyond M, or a B column at or beyond N, only feeds entries
+    // of C that are never stored, so it is read from the tile's first row /
+    // column instead (in bounds; the values do not matter).  An A chunk that
+    // straddles M (M not a multiple of V) is read whole: its elements past row
+    // M-1 are the column's padding or, with a tight lda, the first V-2 rows of
+    // the next column, and again only feed rows that are never stored.  Such
+    // reads stay inside the (K-1)*lda + M elements of A when the column is not
+    // the last one and lda >= V-1, so on the M edge the steady state stops
+    // before the last column (k_whole) and the masked loads take the rest.
+    static_assert(NT % (BM / V) == 0 && NT % KC == 0, "uniform steps between a thread's chunks");
+    // Byte offsets from the tile's first row (A, in the tile's K tile) and
+    // first column (B): A chunk i of tile kt is at a_off + i*a_step from
+    // A + m0 + kt*BK*lda, B chunk i at b_off[i] from B + n0*ldb + kt*BK.
+    // (Formed in 64 bits; they fit 32 when g.buf32 is set, and are unused
+    // otherwise.)
+    const int a_row = m0 + (tid % (BM / V)) * V;
+    constexpr long long TS = sizeof(T);
+    const int a_off =
+        (int)(((long long)(tid / (BM / V)) * lda + (a_row < M ? a_row - m0 : 0)) * TS);
+    constexpr int A_COLS = NT / (BM / V);   // columns of A between a thread's chunks
+    const int a_step = (int)((long long)A_COLS * lda * TS);
+    int b_off[B_LOADS];
+  #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
-      const int q = tid + i * NT;
-      const int nn = q / KC, kk = (q % KC) * V;
-      const int n = n0 + nn, k = k0 + kk;
-      const int valid = (n < N) ? min(K - k, V) : 0;
-      if (valid > 0) rb[i] = load_chunk<TR, VEC>(g.B + (size_t)n * ldb + k, valid);
-      else rb[i] = chunk_t{};
+      const int nn = tid / KC + i * (NT / KC);
+      b_off[i] = (int)(((long long)(n0 + nn < N ? nn : 0) * ldb + (tid % KC) * V) * TS);
     }
-  };
-  auto gload = [&](int kt) {
-    if (g.buf32 && full_mn && (kt + 1) * BK <= K) gload_full(kt);
-    else gload_masked(kt);
-  };
+    const T* const a_tile = g.A + m0;
+    const T* const b_tile = g.B + (size_t)n0 * ldb;
+    const bool straddle = (m0 + BM > M) && (M % V != 0);
+    const bool edge_fast = !straddle || lda >= V - 1;
+    const int k_whole = straddle ? (K - 1) / BK : K / BK;   // whole K tiles the loop may load
+    auto gload_full = [&](int kt) {
+      const __amdgpu_buffer_rsrc_t ar = tile_rsrc(a_tile + (size_t)kt * BK * (size_t)lda);
+  #pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) ra[i] = load_chunk_buf<TR>(ar, a_off, i * a_step);
+      const __amdgpu_buffer_rsrc_t br = tile_rsrc(b_tile + (size_t)kt * BK);
+  #pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) rb[i] = load_chunk_buf<TR>(br, b_off[i], 0);
+    };
+    // Edge tiles and the K tail: out-of-range elements load as zero.
+    auto gload_masked = [&](int kt) {
+      const int k0 = kt * BK;
+  #pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) {
+        const int q = tid + i * NT;
+        const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
+        const int k = k0 + kk, m = m0 + mm;
+        const int valid = (k < K) ? min(M - m, V) : 0;
+        if (valid > 0) ra[i] = load_chunk<TR, VEC>(g.A + (size_t)k * lda + m, valid);
+        else ra[i] = chunk_t{};
+      }
+  #pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int q = tid + i * NT;
+        const int nn = q / KC, kk = (q % KC) * V;
+        const int n = n0 + nn, k = k0 + kk;
+        const int valid = (n < N) ? min(K - k, V) : 0;
+        if (valid > 0) rb[i] = load_chunk<TR, VEC>(g.B + (size_t)n * ldb + k, valid);
+        else rb[i] = chunk_t{};
+      }
+    };
+    auto gload = [&](int kt) {
+      if (g.buf32 && full_mn && (kt + 1) * BK <= K) gload_full(kt);
+      else gload_masked(kt);
+    };
 
-  auto lstore = [&](int stage) {
-    T* As = lds + stage * Cfg::A_STAGE;
-    T* Bs = lds + STAGES * Cfg::A_STAGE + stage * Cfg::B_STAGE;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int q = tid + i * NT;
-      const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
-      *reinterpret_cast<chunk_t*>(As + kk * BM + mm) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int q = tid + i * NT;
-      const int nn = q / KC, kc = q % KC;
-      *reinterpret_cast<chunk_t*>(Bs + nn * BK + ((kc ^ swz<KC, TR::MB>(nn)) * V)) = rb[i];
-    }
-  };
+    auto lstore = [&](int stage) {
+      T* As = lds + stage * Cfg::A_STAGE;
+      T* Bs = lds + STAGES * Cfg::A_STAGE + stage * Cfg::B_STAGE;
+  #pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) {
+        const int q = tid + i * NT;
+        const int kk = q / (BM / V), mm = (q % (BM / V)) * V;
+        *reinterpret_cast<chunk_t*>(As + kk * BM + mm) = ra[i];
+      }
+  #pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int q = tid + i * NT;
+        const int nn = q / KC, kc = q % KC;
+        *reinterpret_cast<chunk_t*>(Bs + nn * BK + ((kc ^ swz<KC, TR::MB>(nn)) * V)) = rb[i];
+      }
+    };
 
-  acc_t acc[RB][CB];
-#pragma unroll
-  for (int b = 0; b < RB; ++b)
-#pragma unroll
-    for (int c = 0; c < CB; ++c) acc[b][c] = acc_t{};
+    acc_t acc[RB][CB];
+  #pragma unroll
+    for (int b = 0; b < RB; ++b)
+  #pragma unroll
+      for (int c = 0; c < CB; ++c) acc[b][c] = acc_t{};
 
-  // Lane roles in the matrix instruction.
-  const int lrow = lane % MB;   // block row (A) / block column (B) of this lane
-  const int kslot = lane / MB;  // which inner-index slot of the instruction
+    // Lane roles in the matrix instruction.
+    const int lrow = lane % MB;   // block row (A) / block column (B) of this lane
+    const int kslot = lane / MB;  // which inner-index slot of the instruction
 
-  // Operands of one group of KG inner indices: CB chunks of B (V inner
-  // indices each) and, for each of the V steps, the RB row values of A.
-  struct GroupOps {
-    chunk_t b[CB];
-    T a[V][RB];
-  };
-  auto read_ops = [&](int stage, int kg, GroupOps& o) {
-    const T* As = lds + stage * Cfg::A_STAGE;
-    const T* Bs = lds + STAGES * Cfg::A_STAGE + stage * Cfg::B_STAGE;
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const int n = wcol + c * MB + lrow;
-      const int kc = kg / V + kslot;
-      o.b[c] = *reinterpret_cast<const chunk_t*>(Bs + n * BK + ((kc ^ swz<KC, TR::MB>(n)) * V));
-    }
-#pragma unroll
-    for (int s = 0; s < V; ++s) {
-      const int k = kg + V * kslot + s;
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-        const T* p = As + k * BM + wrow + sb * MB * W + W * lrow;
-        if constexpr (W == 4) {
-          floatx4 t = *reinterpret_cast<const floatx4*>(p);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o.a[s][sb * W + e] = t[e];
-        } else if constexpr (W == 2) {
-          typedef T T2 __attribute__((ext_vector_type(2)));
-          T2 t = *reinterpret_cast<const T2*>(p);
-          o.a[s][sb * W + 0] = t[0];
-          o.a[s][sb * W + 1] = t[1];
+    // Operands of one group of KG inner indices: CB chunks of B (V inner
+    // indices each) and, for each of the V steps, the RB row values of A.
+    struct GroupOps {
+      chunk_t b[CB];
+      T a[V][RB];
+    };
+    auto read_ops = [&](int stage, int kg, GroupOps& o) {
+      const T* As = lds + stage * Cfg::A_STAGE;
+      const T* Bs = lds + STAGES * Cfg::A_STAGE + stage * Cfg::B_STAGE;
+  #pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int n = wcol + c * MB + lrow;
+        const int kc = kg / V + kslot;
+        o.b[c] = *reinterpret_cast<const chunk_t*>(Bs + n * BK + ((kc ^ swz<KC, TR::MB>(n)) * V));
+      }
+  #pragma unroll
+      for (int s = 0; s < V; ++s) {
+        const int k = kg + V * kslot + s;
+  #pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          const T* p = As + k * BM + wrow + sb * MB * W + W * lrow;
+          if constexpr (W == 4) {
+            floatx4 t = *reinterpret_cast<const floatx4*>(p);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) o.a[s][sb * W + e] = t[e];
+          } else if constexpr (W == 2) {
+            typedef T T2 __attribute__((ext_vector_type(2)));
+            T2 t = *reinterpret_cast<const T2*>(p);
+            o.a[s][sb * W + 0] = t[0];
+            o.a[s][sb * W + 1] = t[1];
+          } else {
+            o.a[s][sb] = p[0];
+          }
+        }
+      }
+    };
+    auto mma = [&](const GroupOps& o) {
+  #pragma unroll
+      for (int s = 0; s < V; ++s)
+  #pragma unroll
+        for (int b = 0; b < RB; ++b)
+  #pragma unroll
+          for (int c = 0; c < CB; ++c) acc[b][c] = TR::mfma(o.a[s][b], o.b[c][s], acc[b][c]);
+    };
+
+    constexpr int NG = BK / KG;      // inner-index groups per K tile
+    constexpr int NGL = NG / KS;     // groups per K tile for one wave
+    const int kg0 = kgrp * NGL * KG; // this wave's first inner index in a tile
+    // This piece's K tiles: [kt_begin, kt_end) (all of them unless stream-K
+    // workgroups share the tile).
+
+    if constexpr (STAGES == 2) {
+      // Two LDS stages.  Tile t+1 is fetched from HBM into registers while
+      // tile t feeds the MFMAs, then written to the other stage; one barrier
+      // per tile.  With one wave per SIMD (256 threads) the operands of group
+      // g+1 are read into a second register set before the MFMAs of group g,
+      // so LDS latency hides behind the same wave's matrix-core work; with more
+      // waves per SIMD the other waves fill those gaps and one set is used.
+      constexpr bool PIPE_OPS = NT <= 256;
+      auto compute = [&](int stage) {
+        if constexpr (PIPE_OPS) {
+          GroupOps ops[2];
+          read_ops(stage, 0, ops[0]);
+  #pragma unroll
+          for (int gi = 0; gi < NG; ++gi) {
+            if (gi + 1 < NG) read_ops(stage, (gi + 1) * KG, ops[(gi + 1) & 1]);
+            // keep the reads above the MFMAs (the scheduler would otherwise
+            // sink each read next to its first use and wait for it there)
+            __builtin_amdgcn_sched_barrier(0);
+            mma(ops[gi & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         } else {
-          o.a[s][sb] = p[0];
+  #pragma unroll
+          for (int gi = 0; gi < NG; ++gi) {
+            GroupOps ops;
+            read_ops(stage, gi * KG, ops);
+            mma(ops);
+          }
         }
-      }
-    }
-  };
-  auto mma = [&](const GroupOps& o) {
-#pragma unroll
-    for (int s = 0; s < V; ++s)
-#pragma unroll
-      for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int c = 0; c < CB; ++c) acc[b][c] = TR::mfma(o.a[s][b], o.b[c][s], acc[b][c]);
-  };
-
-  constexpr int NG = BK / KG;      // inner-index groups per K tile
-  constexpr int NGL = NG / KS;     // groups per K tile for one wave
-  const int kg0 = kgrp * NGL * KG; // this wave's first inner index in a tile
-  // This piece's K tiles: [kt_begin, kt_end) (all of them unless stream-K
-  // workgroups share the tile).
-
-  if constexpr (STAGES == 2) {
-    // Two LDS stages.  Tile t+1 is fetched from HBM into registers while
-    // tile t feeds the MFMAs, then written to the other stage; one barrier
-    // per tile.  With one wave per SIMD (256 threads) the operands of group
-    // g+1 are read into a second register set before the MFMAs of group g,
-    // so LDS latency hides behind the same wave's matrix-core work; with more
-    // waves per SIMD the other waves fill those gaps and one set is used.
-    constexpr bool PIPE_OPS = NT <= 256;
-    auto compute = [&](int stage) {
-      if constexpr (PIPE_OPS) {
-        GroupOps ops[2];
-        read_ops(stage, 0, ops[0]);
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          if (gi + 1 < NG) read_ops(stage, (gi + 1) * KG, ops[(gi + 1) & 1]);
-          // keep the reads above the MFMAs (the scheduler would otherwise
-          // sink each read next to its first use and wait for it there)
-          __builtin_amdgcn_sched_barrier(0);
-          mma(ops[gi & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          GroupOps ops;
-          read_ops(stage, gi * KG, ops);
-          mma(ops);
-        }
-      }
-    };
-    gload(kt_begin);
-    lstore(0);
-    __syncthreads();
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const bool more = kt + 1 < kt_end;
-      if (more) gload(kt + 1);
-      compute((kt - kt_begin) & 1);
-      if (more) lstore((kt + 1 - kt_begin) & 1);
+      };
+      gload(kt_begin);
+      lstore(0);
       __syncthreads();
-    }
-  } else {
-    // Ring of S = STAGES LDS stages, one barrier per tile.  At the top of
-    // iteration kt the registers hold tile kt+S-1 (fetched one iteration
-    // earlier, so HBM latency has a whole tile of MFMA work to hide behind);
-    // they are written to stage (kt+S-1)%S, which last held tile kt-1 and was
-    // released by the previous barrier, and tile kt+S is fetched.  The last
-    // group of tile kt prefetches the operands of group 0 of tile kt+1, which
-    // was written S-2 >= 1 barriers earlier, so the MFMAs of the next tile
-    // start right after the barrier without waiting for LDS.
-    constexpr int S = STAGES;
-    for (int t = 0; t < S - 1; ++t)
-      if (kt_begin + t < kt_end) {
-        gload(kt_begin + t);
-        lstore(t);
+      for (int kt = kt_begin; kt < kt_end; ++kt) {
+        const bool more = kt + 1 < kt_end;
+        if (more) gload(kt + 1);
+        compute((kt - kt_begin) & 1);
+        if (more) lstore((kt + 1 - kt_begin) & 1);
+        __syncthreads();
       }
-    if (kt_begin + S - 1 < kt_end) gload(kt_begin + S - 1);
-    __syncthreads();
-    GroupOps ops[2];
-    read_ops(0, kg0, ops[0]);
-    // Drain those reads so that both edges into the loop header carry no
-    // LDS operations in flight: otherwise the compiler's wait-count
-    // insertion has to assume the prologue's reads are pending at every
-    // iteration and makes the first MFMAs wait for the tile's LDS stores.
-    // (s_waitcnt lgkmcnt(0); the vector-memory and export counts at their
-    // no-wait maxima.)
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    // Instruction counts of one iteration, for the interleave below.
-    constexpr int N_RD = CB + V * SB;                              // ds_read per group
-    constexpr int N_WR = A_LOADS + B_LOADS;                        // ds_write
-    constexpr int N_LD = A_LOADS + B_LOADS;                        // global loads
-    constexpr int MPG = V * RB * CB;                                // MFMAs per group
-    constexpr bool INTERLEAVE = NGL >= 2 && MPG >= N_WR + N_LD;
-    // Operand reads too, one between MFMAs, when a group has room for them.
-    // After each barrier every wave starts the same group at once; reads
-    // issued as a block then queue behind the other waves' reads, and both
-    // waves of a SIMD stall with the matrix core idle.
-    constexpr bool READS_SPREAD = MPG >= N_RD;
-    constexpr bool RIL = INTERLEAVE && MPG >= N_RD + N_WR + N_LD;
-    // Schedule: the operand reads of the next group one per MFMA, then the
-    // rest of the group's MFMAs (groups without stores or loads).
-    auto spread_reads = [&]() {
-      if constexpr (READS_SPREAD) {
-#pragma unroll
-        for (int i = 0; i < N_RD; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    } else {
+      // Ring of S = STAGES LDS stages, one barrier per tile.  At the top of
+      // iteration kt the registers hold tile kt+S-1 (fetched one iteration
+      // earlier, so HBM latency has a whole tile of MFMA work to hide behind);
+      // they are written to stage (kt+S-1)%S, which last held tile kt-1 and was
+      // released by the previous barrier, and tile kt+S is fetched.  The last
+      // group of tile kt prefetches the operands of group 0 of tile kt+1, which
+      // was written S-2 >= 1 barriers earlier, so the MFMAs of the next tile
+      // start right after the barrier without waiting for LDS.
+      constexpr int S = STAGES;
+      for (int t = 0; t < S - 1; ++t)
+        if (kt_begin + t < kt_end) {
+          gload(kt_begin + t);
+          lstore(t);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MPG - N_RD, 0);
-      }
-    };
-    int st = 0;                       // stage of tile kt
-    int kt = kt_begin;
-    // Steady state, while tile kt+S exists and is whole (edge tiles too,
-    // with the redirected loads above): one branch-free block per iteration.  With in-order issue,
-    // the next group's operand reads, the tile's LDS stores and its global
-    // loads are spread evenly between group 0's MFMAs (each executes while
-    // an MFMA occupies the matrix core) instead of running as a block while
-    // the matrix core idles.
-    const int kt_fast_end = (INTERLEAVE && edge_fast && g.buf32)
-                                ? max(kt_begin, min(kt_end, k_whole) - S)
-                                : kt_begin;
-    // The steady state is unrolled by S, so that every stage index is a
-    // compile-time constant and each LDS access is a per-thread base plus an
-    // immediate offset (no address arithmetic per iteration).
-    auto fast_iteration = [&](const int st, const int kt) __attribute__((always_inline)) {
-      const int st_next = (st + 1 == S) ? 0 : st + 1;
-      const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
-      read_ops(st, kg0 + KG, ops[1]);
-      if constexpr (!RIL) __builtin_amdgcn_sched_barrier(0);
-      lstore(st_store);
-      gload_full(kt + S);
-      mma(ops[0]);
-      if constexpr (INTERLEAVE) {
-        // spread evenly: SP MFMAs before each read, store and load
-        constexpr int NM = (RIL ? N_RD : 0) + N_WR + N_LD;
-        constexpr int SP = MPG / NM;
-        if constexpr (RIL) {
-#pragma unroll
+      if (kt_begin + S - 1 < kt_end) gload(kt_begin + S - 1);
+      __syncthreads();
+      GroupOps ops[2];
+      read_ops(0, kg0, ops[0]);
+      // Drain those reads so that both edges into the loop header carry no
+      // LDS operations in flight: otherwise the compiler's wait-count
+      // insertion has to assume the prologue's reads are pending at every
+      // iteration and makes the first MFMAs wait for the tile's LDS stores.
+      // (s_waitcnt lgkmcnt(0); the vector-memory and export counts at their
+      // no-wait maxima.)
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      // Instruction counts of one iteration, for the interleave below.
+      constexpr int N_RD = CB + V * SB;                              // ds_read per group
+      constexpr int N_WR = A_LOADS + B_LOADS;                        // ds_write
+      constexpr int N_LD = A_LOADS + B_LOADS;                        // global loads
+      constexpr int MPG = V * RB * CB;                                // MFMAs per group
+      constexpr bool INTERLEAVE = NGL >= 2 && MPG >= N_WR + N_LD;
+      // Operand reads too, one between MFMAs, when a group has room for them.
+      // After each barrier every wave starts the same group at once; reads
+      // issued as a block then queue behind the other waves' reads, and both
+      // waves of a SIMD stall with the matrix core idle.
+      constexpr bool READS_SPREAD = MPG >= N_RD;
+      constexpr bool RIL = INTERLEAVE && MPG >= N_RD + N_WR + N_LD;
+      // Schedule: the operand reads of the next group one per MFMA, then the
+      // rest of the group's MFMAs (groups without stores or loads).
+      auto spread_reads = [&]() {
+        if constexpr (READS_SPREAD) {
+  #pragma unroll
           for (int i = 0; i < N_RD; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
           }
+          __builtin_amdgcn_sched_group_barrier(0x008, MPG - N_RD, 0);
         }
-#pragma unroll
-        for (int i = 0; i < N_WR; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-        }
-#pragma unroll
-        for (int i = 0; i < N_LD; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, MPG - SP * NM, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int gi = 1; gi < NGL; ++gi) {
-        // the next tile (kt+1 < kt_fast_end + S <= kt_end) always exists here
-        if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
-        else read_ops(st_next, kg0, ops[(gi + 1) & 1]);
-        if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
-        mma(ops[gi & 1]);
-        spread_reads();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __syncthreads();
-    };
-    // st == 0 here (kt == kt_begin), and after every S iterations
-    if constexpr (Cfg::UNROLL) {
-      for (; kt + S <= kt_fast_end; kt += S)
-        static_for<0, S>([&](auto st_c) {
-          fast_iteration(decltype(st_c)::value, kt + decltype(st_c)::value);
-        });
-    }
-    for (; kt < kt_fast_end; ++kt) {
-      fast_iteration(st, kt);
-      st = (st + 1 == S) ? 0 : st + 1;
-    }
-    // Remaining iterations (edge tiles, the K tail, the last S tiles).
-    for (; kt < kt_end; ++kt) {
-      const int st_next = (st + 1 == S) ? 0 : st + 1;
-      const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
-      // At the last tile the prefetch re-reads this tile's own stage (in
-      // bounds, unused): a branch here would make the compiler wait for the
-      // prefetch before the current group's MFMAs.
-      const int st_pf = (kt + 1 < kt_end) ? st_next : st;
-      if (kt + S - 1 < kt_end) lstore(st_store);
-      if (kt + S < kt_end) gload(kt + S);
-#pragma unroll
-      for (int gi = 0; gi < NGL; ++gi) {
-        if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
-        else read_ops(st_pf, kg0, ops[(gi + 1) & 1]);
-        if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
-        mma(ops[gi & 1]);
-        spread_reads();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __syncthreads();
-      st = st_next;
-    }
-  }
-
-  if constexpr (KS == 2) {
-    // Group 1 hands its partial sums to group 0 through LDS (lane-linear,
-    // so each register index is one contiguous 256-byte row per wave); group
-    // 0 adds them in a fixed order and runs the epilogue alone.
-    constexpr int NREG = RB * CB * TR::NACC;
-    __syncthreads();                       // every wave is done with the ring
-    T* red = lds + wave_in * NREG * 64 + lane;
-    if (kgrp == 1) {
-#pragma unroll
-      for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int c = 0; c < CB; ++c)
-#pragma unroll
-          for (int e = 0; e < TR::NACC; ++e) red[((b * CB + c) * TR::NACC + e) * 64] = acc[b][c][e];
-    }
-    __syncthreads();
-    if (kgrp == 0) {
-#pragma unroll
-      for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int c = 0; c < CB; ++c)
-#pragma unroll
-          for (int e = 0; e < TR::NACC; ++e) acc[b][c][e] += red[((b * CB + c) * TR::NACC + e) * 64];
-    }
-    // the epilogue's staging reuses this LDS: every read of it is done first
-    __syncthreads();
-    if (kgrp == 1) return;
-  }
-
-  // Destination: C, or for a stream-K piece its raw partial sums (alpha = 1,
-  // beta = 0, all BM x BN elements, column-major with ld = BM) in workspace
-  // slot `slot`.
-  const bool to_ws = slot >= 0;
-  T* const cbase = to_ws ? g.ws + (size_t)slot * (BM * BN) : g.C;
-  const int ldc = to_ws ? BM : g.ldc;
-  const T alpha = to_ws ? T(1) : g.alpha, beta = to_ws ? T(0) : g.beta;
-  const bool read_c = beta != T(0);
-  constexpr int RUN = TR::RUN_R * W;
-  constexpr int NRUN = TR::NACC / TR::RUN_R;
-  // A lane's accumulator registers come in runs of RUN_R consecutive block
-  // rows (see the trait).  Block b = sb*W + b' puts block row i at wave-tile
-  // row sb*MB*W + W*i + b', so for fixed (c, sb, run) the lane owns RUN =
-  // RUN_R*W consecutive rows of one column: element o of that run is
-  // register run*RUN_R + o/W of block sb*W + o%W.
-  if constexpr (Cfg::STAGED_EPI) {
-    // Staged through LDS so that global memory sees whole column segments.
-    // Per column block c, each wave writes its MB columns x WM rows to a
-    // private LDS region, then reads it back a 16-byte chunk per lane with
-    // consecutive lanes on consecutive rows: a wave's store covers whole
-    // columns (WM*sizeof(T) bytes each) instead of 16 bytes in each of 32
-    // columns.  Chunk h of column j sits at chunk h ^ (j & 7) of the column's
-    // WM/V chunks: the 8 lanes of a ds_write_b128 cycle (8 consecutive
-    // columns, one chunk index) then hit 8 distinct bank groups, and each read
-    // cycle (8-lane blocks b and b^3) covers 16 distinct groups of a 256-byte
-    // line.  Only this wave touches its region, and a wave's LDS operations
-    // complete in order, so no barrier is needed.
-    const int m_end = to_ws ? BM : M, n_end = to_ws ? BN : N;   // extent in that frame
-    const int row_base = (to_ws ? 0 : m0) + wrow, col_base = (to_ws ? 0 : n0) + wcol;
-    constexpr int LDW = Cfg::EPI_LDW;            // staging column stride (elements)
-    constexpr int CPC = Cfg::WM / V;             // chunks per wave-tile column
-    constexpr int NCH = MB * CPC;                // chunks per column block
-    static_assert(RUN % V == 0, "a run is whole 16-byte chunks");
-    static_assert(NCH % 64 == 0, "whole chunks per lane");
-    T* const stg = lds + wave_in * (MB * LDW);
-    // With beta != 0 and the whole tile inside C, the old C of column block
-    // c+1 is loaded as soon as block c is staged (its accumulators are free
-    // then), so that its HBM latency passes while block c is stored; block
-    // 0's loads go out before its staging.
-    constexpr int NI = NCH / 64;                 // chunks per lane per column block
-    const bool pre_c = read_c && !to_ws && full_mn;
-    chunk_t cpre[2][NI];
-    auto load_c_block = [&](int c, chunk_t (&dst)[NI]) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int q = lane + 64 * i;
-        const int col = q / CPC, rc = q % CPC;
-        dst[i] = load_chunk_full<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc +
-                                          (row_base + rc * V));
-      }
-    };
-    if (pre_c) load_c_block(0, cpre[0]);
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-#pragma unroll
-        for (int run = 0; run < NRUN; ++run) {
-          T* const pcol = stg + lrow * LDW;
-          const int ch0 = (sb * MB * W + W * TR::irow(run, kslot)) / V;
-#pragma unroll
-          for (int h = 0; h < RUN / V; ++h) {
-            chunk_t v;
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-              const int o = h * V + e;
-              v[e] = acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+      };
+      int st = 0;                       // stage of tile kt
+      int kt = kt_begin;
+      // Steady state, while tile kt+S exists and is whole (edge tiles too,
+      // with the redirected loads above): one branch-free block per
+      // iteration.  With in-order issue, the next group's operand reads, the
+      // tile's LDS stores and its global loads are spread evenly between
+      // group 0's MFMAs (each executes while an MFMA occupies the matrix
+      // core) instead of running as a block while the matrix core idles.
+      const int kt_fast_end = (INTERLEAVE && edge_fast && g.buf32)
+                                  ? max(kt_begin, min(kt_end, k_whole) - S)
+                                  : kt_begin;
+      // The steady state is unrolled by S, so that every stage index is a
+      // compile-time constant and each LDS access is a per-thread base plus an
+      // immediate offset (no address arithmetic per iteration).
+      auto fast_iteration = [&](const int st, const int kt) __attribute__((always_inline)) {
+        const int st_next = (st + 1 == S) ? 0 : st + 1;
+        const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
+        read_ops(st, kg0 + KG, ops[1]);
+        if constexpr (!RIL) __builtin_amdgcn_sched_barrier(0);
+        lstore(st_store);
+        gload_full(kt + S);
+        mma(ops[0]);
+        if constexpr (INTERLEAVE) {
+          // spread evenly: SP MFMAs before each read, store and load
+          constexpr int NM = (RIL ? N_RD : 0) + N_WR + N_LD;
+          constexpr int SP = MPG / NM;
+          if constexpr (RIL) {
+  #pragma unroll
+            for (int i = 0; i < N_RD; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
             }
-            *reinterpret_cast<chunk_t*>(pcol + ((ch0 + h) ^ (lrow & 7)) * V) = v;
           }
+  #pragma unroll
+          for (int i = 0; i < N_WR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+          }
+  #pragma unroll
+          for (int i = 0; i < N_LD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, MPG - SP * NM, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int gi = 1; gi < NGL; ++gi) {
+          // the next tile (kt+1 < kt_fast_end + S <= kt_end) always exists here
+          if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
+          else read_ops(st_next, kg0, ops[(gi + 1) & 1]);
+          if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
+          mma(ops[gi & 1]);
+          spread_reads();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+      };
+      // st == 0 here (kt == kt_begin), and after every S iterations
+      if constexpr (Cfg::UNROLL) {
+        for (; kt + S <= kt_fast_end; kt += S)
+          static_for<0, S>([&](auto st_c) {
+            fast_iteration(decltype(st_c)::value, kt + decltype(st_c)::value);
+          });
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the staging is written
-      if (pre_c) {
-        if (c + 1 < CB) load_c_block(c + 1, cpre[(c + 1) & 1]);
-#pragma unroll
+      for (; kt < kt_fast_end; ++kt) {
+        fast_iteration(st, kt);
+        st = (st + 1 == S) ? 0 : st + 1;
+      }
+      // Remaining iterations (edge tiles, the K tail, the last S tiles).
+      for (; kt < kt_end; ++kt) {
+        const int st_next = (st + 1 == S) ? 0 : st + 1;
+        const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
+        // At the last tile the prefetch re-reads this tile's own stage (in
+        // bounds, unused): a branch here would make the compiler wait for the
+        // prefetch before the current group's MFMAs.
+        const int st_pf = (kt + 1 < kt_end) ? st_next : st;
+        if (kt + S - 1 < kt_end) lstore(st_store);
+        if (kt + S < kt_end) gload(kt + S);
+  #pragma unroll
+        for (int gi = 0; gi < NGL; ++gi) {
+          if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
+          else read_ops(st_pf, kg0, ops[(gi + 1) & 1]);
+          if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
+          mma(ops[gi & 1]);
+          spread_reads();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        st = st_next;
+      }
+    }
+
+    if constexpr (KS == 2) {
+      // Group 1 hands its partial sums to group 0 through LDS (lane-linear,
+      // so each register index is one contiguous 256-byte row per wave); group
+      // 0 adds them in a fixed order and runs the epilogue alone.
+      constexpr int NREG = RB * CB * TR::NACC;
+      __syncthreads();                       // every wave is done with the ring
+      T* red = lds + wave_in * NREG * 64 + lane;
+      if (kgrp == 1) {
+  #pragma unroll
+        for (int b = 0; b < RB; ++b)
+  #pragma unroll
+          for (int c = 0; c < CB; ++c)
+  #pragma unroll
+            for (int e = 0; e < TR::NACC; ++e) red[((b * CB + c) * TR::NACC + e) * 64] = acc[b][c][e];
+      }
+      __syncthreads();
+      if (kgrp == 0) {
+  #pragma unroll
+        for (int b = 0; b < RB; ++b)
+  #pragma unroll
+          for (int c = 0; c < CB; ++c)
+  #pragma unroll
+            for (int e = 0; e < TR::NACC; ++e) acc[b][c][e] += red[((b * CB + c) * TR::NACC + e) * 64];
+      }
+      // the epilogue's staging reuses this LDS: every read of it is done first
+      __syncthreads();
+      if (kgrp == 1) return;
+    }
+
+    // Destination: C, or for a stream-K piece its raw partial sums (alpha = 1,
+    // beta = 0, all BM x BN elements, column-major with ld = BM) in workspace
+    // slot `slot`.
+    const bool to_ws = slot >= 0;
+    T* const cbase = to_ws ? g.ws + (size_t)slot * (BM * BN) : g.C;
+    const int ldc = to_ws ? BM : g.ldc;
+    const T alpha = to_ws ? T(1) : g.alpha, beta = to_ws ? T(0) : g.beta;
+    const bool read_c = beta != T(0);
+    constexpr int RUN = TR::RUN_R * W;
+    constexpr int NRUN = TR::NACC / TR::RUN_R;
+    // A lane's accumulator registers come in runs of RUN_R consecutive block
+    // rows (see the trait).  Block b = sb*W + b' puts block row i at wave-tile
+    // row sb*MB*W + W*i + b', so for fixed (c, sb, run) the lane owns RUN =
+    // RUN_R*W consecutive rows of one column: element o of that run is
+    // register run*RUN_R + o/W of block sb*W + o%W.
+    if constexpr (Cfg::STAGED_EPI) {
+      // Staged through LDS so that global memory sees whole column segments.
+      // Per column block c, each wave writes its MB columns x WM rows to a
+      // private LDS region, then reads it back a 16-byte chunk per lane with
+      // consecutive lanes on consecutive rows: a wave's store covers whole
+      // columns (WM*sizeof(T) bytes each) instead of 16 bytes in each of 32
+      // columns.  Chunk h of column j sits at chunk h ^ (j & 7) of the column's
+      // WM/V chunks: the 8 lanes of a ds_write_b128 cycle (8 consecutive
+      // columns, one chunk index) then hit 8 distinct bank groups, and each read
+      // cycle (8-lane blocks b and b^3) covers 16 distinct groups of a 256-byte
+      // line.  Only this wave touches its region, and a wave's LDS operations
+      // complete in order, so no barrier is needed.
+      const int m_end = to_ws ? BM : M, n_end = to_ws ? BN : N;   // extent in that frame
+      const int row_base = (to_ws ? 0 : m0) + wrow, col_base = (to_ws ? 0 : n0) + wcol;
+      constexpr int LDW = Cfg::EPI_LDW;            // staging column stride (elements)
+      constexpr int CPC = Cfg::WM / V;             // chunks per wave-tile column
+      constexpr int NCH = MB * CPC;                // chunks per column block
+      static_assert(RUN % V == 0, "a run is whole 16-byte chunks");
+      static_assert(NCH % 64 == 0, "whole chunks per lane");
+      T* const stg = lds + wave_in * (MB * LDW);
+      // With beta != 0 and the whole tile inside C, the old C of column block
+      // c+1 is loaded as soon as block c is staged (its accumulators are free
+      // then), so that its HBM latency passes while block c is stored; block
+      // 0's loads go out before its staging.
+      constexpr int NI = NCH / 64;                 // chunks per lane per column block
+      const bool pre_c = read_c && !to_ws && full_mn;
+      chunk_t cpre[2][NI];
+      auto load_c_block = [&](int c, chunk_t (&dst)[NI]) {
+  #pragma unroll
         for (int i = 0; i < NI; ++i) {
           const int q = lane + 64 * i;
           const int col = q / CPC, rc = q % CPC;
-          const chunk_t v =
-              *reinterpret_cast<const chunk_t*>(stg + col * LDW + (rc ^ (col & 7)) * V);
-          chunk_t out;
-#pragma unroll
-          for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cpre[c & 1][i][e], alpha * v[e]);
-          store_chunk<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc + (row_base + rc * V),
-                               out);
+          dst[i] = load_chunk_full<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc +
+                                            (row_base + rc * V));
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the region is reused
-        continue;
-      }
-#pragma unroll
-      for (int i = 0; i < NCH / 64; ++i) {
-        const int q = lane + 64 * i;
-        const int col = q / CPC, rc = q % CPC;
-        const chunk_t v = *reinterpret_cast<const chunk_t*>(stg + col * LDW + (rc ^ (col & 7)) * V);
-        const int gcol = col_base + c * MB + col, grow = row_base + rc * V;
-        if (gcol < n_end) {
-          T* pc = cbase + (size_t)gcol * ldc + grow;
-          if (grow + V <= m_end) {
-            chunk_t out;
-            if (read_c) {
-              const chunk_t cv = load_chunk_full<TR, VEC>(pc);
-#pragma unroll
-              for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cv[e], alpha * v[e]);
-            } else {
-#pragma unroll
-              for (int e = 0; e < V; ++e) out[e] = alpha * v[e];
+      };
+      if (pre_c) load_c_block(0, cpre[0]);
+  #pragma unroll
+      for (int c = 0; c < CB; ++c) {
+  #pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+  #pragma unroll
+          for (int run = 0; run < NRUN; ++run) {
+            T* const pcol = stg + lrow * LDW;
+            const int ch0 = (sb * MB * W + W * TR::irow(run, kslot)) / V;
+  #pragma unroll
+            for (int h = 0; h < RUN / V; ++h) {
+              chunk_t v;
+  #pragma unroll
+              for (int e = 0; e < V; ++e) {
+                const int o = h * V + e;
+                v[e] = acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+              }
+              *reinterpret_cast<chunk_t*>(pcol + ((ch0 + h) ^ (lrow & 7)) * V) = v;
             }
-            store_chunk<TR, VEC>(pc, out);
-          } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-              if (grow + e < m_end) {
-                T o = alpha * v[e];
-                if (read_c) o = __builtin_fma(beta, pc[e], o);
-                pc[e] = o;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the staging is written
+        if (pre_c) {
+          if (c + 1 < CB) load_c_block(c + 1, cpre[(c + 1) & 1]);
+  #pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const int q = lane + 64 * i;
+            const int col = q / CPC, rc = q % CPC;
+            const chunk_t v =
+                *reinterpret_cast<const chunk_t*>(stg + col * LDW + (rc ^ (col & 7)) * V);
+            chunk_t out;
+  #pragma unroll
+            for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cpre[c & 1][i][e], alpha * v[e]);
+            store_chunk<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc + (row_base + rc * V),
+                                 out);
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the region is reused
+          continue;
+        }
+  #pragma unroll
+        for (int i = 0; i < NCH / 64; ++i) {
+          const int q = lane + 64 * i;
+          const int col = q / CPC, rc = q % CPC;
+          const chunk_t v = *reinterpret_cast<const chunk_t*>(stg + col * LDW + (rc ^ (col & 7)) * V);
+          const int gcol = col_base + c * MB + col, grow = row_base + rc * V;
+          if (gcol < n_end) {
+            T* pc = cbase + (size_t)gcol * ldc + grow;
+            if (grow + V <= m_end) {
+              chunk_t out;
+              if (read_c) {
+                const chunk_t cv = load_chunk_full<TR, VEC>(pc);
+  #pragma unroll
+                for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cv[e], alpha * v[e]);
+              } else {
+  #pragma unroll
+                for (int e = 0; e < V; ++e) out[e] = alpha * v[e];
+              }
+              store_chunk<TR, VEC>(pc, out);
+            } else {
+  #pragma unroll
+              for (int e = 0; e < V; ++e) {
+                if (grow + e < m_end) {
+                  T o = alpha * v[e];
+                  if (read_c) o = __builtin_fma(beta, pc[e], o);
+                  pc[e] = o;
+                }
               }
             }
           }
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the region is reused
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the region is reused
-    }
-  } else {
-    // Direct stores from the accumulator registers: runs of RUN rows of a
-    // column per lane, 16-byte stores where whole chunks.
-    const bool full_out = to_ws || full_mn;
-    const int row_off = to_ws ? 0 : m0, col_off = to_ws ? 0 : n0;
-    constexpr bool VEC_C = (RUN % V == 0);   // whole 16-byte chunks per run
-    // The old C of group (c, sb): NRUN runs of RUN rows of this lane's column.
-    auto load_c_group = [&](int c, int sb, T (&cv)[NRUN][RUN]) {
-      const T* pcol = cbase + (size_t)(col_off + wcol + c * MB + lrow) * ldc;
-      const int row0 = row_off + wrow + sb * MB * W;
-#pragma unroll
-      for (int run = 0; run < NRUN; ++run) {
-        const T* pc = pcol + row0 + W * TR::irow(run, kslot);
-        if constexpr (VEC_C) {
-#pragma unroll
-          for (int h = 0; h < RUN / V; ++h) {
-            chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
-#pragma unroll
-            for (int e = 0; e < V; ++e) cv[run][h * V + e] = v[e];
-          }
-        } else {
-#pragma unroll
-          for (int o = 0; o < RUN; ++o) cv[run][o] = pc[o];
-        }
-      }
-    };
-    if (read_c && full_mn && !to_ws) {
-      // Whole tile inside C with beta != 0: the old C of the next group is
-      // loaded before this group's multiply-adds and stores, so that one
-      // HBM latency is exposed per tile instead of one per group.
-      constexpr int NG_EPI = CB * SB;
-      T cvb[2][NRUN][RUN];
-      load_c_group(0, 0, cvb[0]);
-#pragma unroll
-      for (int gq = 0; gq < NG_EPI; ++gq) {
-        const int c = gq / SB, sb = gq % SB;
-        if (gq + 1 < NG_EPI) load_c_group((gq + 1) / SB, (gq + 1) % SB, cvb[(gq + 1) & 1]);
-        T* pcol = cbase + (size_t)(col_off + wcol + c * MB + lrow) * ldc;
+    } else {
+      // Direct stores from the accumulator registers: runs of RUN rows of a
+      // column per lane, 16-byte stores where whole chunks.
+      const bool full_out = to_ws || full_mn;
+      const int row_off = to_ws ? 0 : m0, col_off = to_ws ? 0 : n0;
+      constexpr bool VEC_C = (RUN % V == 0);   // whole 16-byte chunks per run
+      // The old C of group (c, sb): NRUN runs of RUN rows of this lane's column.
+      auto load_c_group = [&](int c, int sb, T (&cv)[NRUN][RUN]) {
+        const T* pcol = cbase + (size_t)(col_off + wcol + c * MB + lrow) * ldc;
         const int row0 = row_off + wrow + sb * MB * W;
-#pragma unroll
+  #pragma unroll
         for (int run = 0; run < NRUN; ++run) {
-          T* pc = pcol + row0 + W * TR::irow(run, kslot);
-          T out[RUN];
-#pragma unroll
-          for (int o = 0; o < RUN; ++o)
-            out[o] = __builtin_fma(beta, cvb[gq & 1][run][o],
-                                   alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W]);
+          const T* pc = pcol + row0 + W * TR::irow(run, kslot);
           if constexpr (VEC_C) {
-#pragma unroll
+  #pragma unroll
             for (int h = 0; h < RUN / V; ++h) {
-              chunk_t v;
-#pragma unroll
-              for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
-              store_chunk<TR, VEC>(pc + h * V, v);
+              chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
+  #pragma unroll
+              for (int e = 0; e < V; ++e) cv[run][h * V + e] = v[e];
             }
           } else {
-#pragma unroll
-            for (int o = 0; o < RUN; ++o) pc[o] = out[o];
+  #pragma unroll
+            for (int o = 0; o < RUN; ++o) cv[run][o] = pc[o];
           }
         }
-      }
-      return;
-    }
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const int col = col_off + wcol + c * MB + lrow;
-      T* pcol = cbase + (size_t)col * ldc;
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-        const int row0 = row_off + wrow + sb * MB * W;
-        if (full_out) {
-          // Whole tile in range: issue every C load of this column block
-          // first, then the multiply-adds and stores, so that the loads'
-          // latency is paid once rather than once per run.
-          T cv[NRUN][RUN];
-          if (read_c) load_c_group(c, sb, cv);
-#pragma unroll
+      };
+      if (read_c && full_mn && !to_ws) {
+        // Whole tile inside C with beta != 0: the old C of the next group is
+        // loaded before this group's multiply-adds and stores, so that one
+        // HBM latency is exposed per tile instead of one per group.
+        constexpr int NG_EPI = CB * SB;
+        T cvb[2][NRUN][RUN];
+        load_c_group(0, 0, cvb[0]);
+  #pragma unroll
+        for (int gq = 0; gq < NG_EPI; ++gq) {
+          const int c = gq / SB, sb = gq % SB;
+          if (gq + 1 < NG_EPI) load_c_group((gq + 1) / SB, (gq + 1) % SB, cvb[(gq + 1) & 1]);
+          T* pcol = cbase + (size_t)(col_off + wcol + c * MB + lrow) * ldc;
+          const int row0 = row_off + wrow + sb * MB * W;
+  #pragma unroll
           for (int run = 0; run < NRUN; ++run) {
             T* pc = pcol + row0 + W * TR::irow(run, kslot);
             T out[RUN];
-#pragma unroll
-            for (int o = 0; o < RUN; ++o) {
-              out[o] = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
-              if (read_c) out[o] = __builtin_fma(beta, cv[run][o], out[o]);
-            }
+  #pragma unroll
+            for (int o = 0; o < RUN; ++o)
+              out[o] = __builtin_fma(beta, cvb[gq & 1][run][o],
+                                     alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W]);
             if constexpr (VEC_C) {
-#pragma unroll
+  #pragma unroll
               for (int h = 0; h < RUN / V; ++h) {
                 chunk_t v;
-#pragma unroll
+  #pragma unroll
                 for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
                 store_chunk<TR, VEC>(pc + h * V, v);
               }
             } else {
-#pragma unroll
+  #pragma unroll
               for (int o = 0; o < RUN; ++o) pc[o] = out[o];
             }
           }
-        } else if (col < N) {
-          // Edge tile: element-wise bounds checks.
-#pragma unroll
-          for (int run = 0; run < NRUN; ++run) {
-            const int row = row0 + W * TR::irow(run, kslot);
-            T* pc = pcol + row;
-#pragma unroll
-            for (int o = 0; o < RUN; ++o) {
-              if (row + o < M) {
-                T v = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
-                if (read_c) v = __builtin_fma(beta, pc[o], v);
-                pc[o] = v;
+        }
+        return;
+      }
+  #pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int col = col_off + wcol + c * MB + lrow;
+        T* pcol = cbase + (size_t)col * ldc;
+  #pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          const int row0 = row_off + wrow + sb * MB * W;
+          if (full_out) {
+            // Whole tile in range: issue every C load of this column block
+            // first, then the multiply-adds and stores, so that the loads'
+            // latency is paid once rather than once per run.
+            T cv[NRUN][RUN];
+            if (read_c) load_c_group(c, sb, cv);
+  #pragma unroll
+            for (int run = 0; run < NRUN; ++run) {
+              T* pc = pcol + row0 + W * TR::irow(run, kslot);
+              T out[RUN];
+  #pragma unroll
+              for (int o = 0; o < RUN; ++o) {
+                out[o] = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+                if (read_c) out[o] = __builtin_fma(beta, cv[run][o], out[o]);
+              }
+              if constexpr (VEC_C) {
+  #pragma unroll
+                for (int h = 0; h < RUN / V; ++h) {
+                  chunk_t v;
+  #pragma unroll
+                  for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
+                  store_chunk<TR, VEC>(pc + h * V, v);
+                }
+              } else {
+  #pragma unroll
+                for (int o = 0; o < RUN; ++o) pc[o] = out[o];
+              }
+            }
+          } else if (col < N) {
+            // Edge tile: element-wise bounds checks.
+  #pragma unroll
+            for (int run = 0; run < NRUN; ++run) {
+              const int row = row0 + W * TR::irow(run, kslot);
+              T* pc = pcol + row;
+  #pragma unroll
+              for (int o = 0; o < RUN; ++o) {
+                if (row + o < M) {
+                  T v = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
+                  if (read_c) v = __builtin_fma(beta, pc[o], v);
+                  pc[o] = v;
+                }
               }
             }
           }
         }
       }
     }
-  }
   };  // tile_piece
 
   if constexpr (!SKP) {
