@@ -10,6 +10,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -183,6 +184,40 @@ def test_selection_with_workspace():
     # invalid arguments: the same status as the plain selector, no stream-K
     bad = (4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4)
     assert pg.select_ws_f32(*bad, 1 << 20) == (-6, 0, 0)
+
+
+def test_plan_invariants_on_random_shapes():
+    """Host logic only: for seeded random shapes, the plan the workspace
+    entry point reports is consistent with the tiling it names (256 compute
+    units, the fallback without a GPU): the workspace holds two tiles of
+    partial sums per stream-K workgroup; stream-K workgroups outnumber the
+    leftover tiles, at most one per compute unit, each with at least 4 K
+    tiles after a full round (2 without one); strip rows are the 1 to 8 rows
+    below whole tile rows; without a workspace the choice is the plain one."""
+    rng = np.random.default_rng(8)
+    for t in range(400):
+        f32 = t % 3 != 0
+        m, n = (int(x) for x in rng.integers(1, 9000, 2))
+        k = int(rng.integers(1, 4000))
+        sel = pg.select_ws_f32 if f32 else pg.select_ws_f64
+        plain = pg.select_f32 if f32 else pg.select_f64
+        size = 4 if f32 else 8
+        args = (m, n, k, 1.0, FAKE, m, FAKE, k, 0.0, FAKE, m)
+        ws = (pg.workspace_f32 if f32 else pg.workspace_f64)(m, n, k)
+        v, sk, strip = sel(*args, ws)
+        bm, bn, bk = (int(x) for x in re.match(r"f\d\d_(\d+)x(\d+)x(\d+)", name_of(v)).groups())
+        if strip:
+            assert 1 <= strip <= 8 and (m - strip) % bm == 0 and m > bm, (m, n, k, strip)
+        tiles = -(-(m - strip) // bm) * -(-n // bn)
+        rest = tiles % 256
+        if sk:
+            assert ws == 2 * sk * bm * bn * size
+            assert rest > 0 and rest < sk <= 256, (m, n, k, sk, rest)
+            assert rest * -(-k // bk) // sk >= (4 if tiles >= 256 else 2)
+        else:
+            assert ws == 0
+        v0, sk0, strip0 = sel(*args, 0)
+        assert v0 == plain(*args) and sk0 == 0
 
 
 def test_device_info_argument_codes():
