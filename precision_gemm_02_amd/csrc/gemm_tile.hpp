@@ -955,9 +955,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   if constexpr (!SKP) {
     tile_piece(xcd_remap(blockIdx.x, g.full_tiles), 0, nk_all, -1);
   } else {
-    // (the K-group hand-over's early exit would break the barrier between
-    // pieces)
-    static_assert(KS == 1, "stream-K pieces need one K group");
+    // With two K groups, group 1 leaves a piece after the hand-over (both
+    // groups have passed the same barriers) while group 0 runs the
+    // epilogue, which has none; both meet again at the barrier below.
     for (int pc = 0; pc < npieces; ++pc) {
       int t_lin, kb = 0, ke = nk_all, slot = -1;
       if (!sk_wg) {

@@ -20,6 +20,9 @@ namespace pgemm {
 #define PGEMM_F32_K2(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                          \
   {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, false, \
    &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2>}
+#define PGEMM_F32_K2_SK(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                      \
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, true, \
+   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2, true>}
 
 // A host function owns the table so that it is never treated as device data.
 const Variant<float>* f32_variants(int* count) {
@@ -57,8 +60,8 @@ const Variant<float>* f32_variants(int* count) {
       // 64 x 64 tiles with two K groups of 4 waves (8 waves, two per SIMD)
       // on a ring of 3 stages of BK 32: long K loops on few tiles per
       // compute unit, where one wave per SIMD cannot hide the memory latency
-      PGEMM_F32_K2(64, 64, 32, 2, 2, 3, true, vec),
-      PGEMM_F32_K2(64, 64, 32, 2, 2, 3, false, ua),
+      PGEMM_F32_K2_SK(64, 64, 32, 2, 2, 3, true, vec),
+      PGEMM_F32_K2_SK(64, 64, 32, 2, 2, 3, false, ua),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -470,6 +470,10 @@ SK_SHAPES = [
     (np.float32, 2885, 68, 1923),      # 92 edge tiles, crossing, K tail 3
     (np.float64, 65, 2145, 1849),      # 68 fp64 edge tiles, crossing, K tail 9
     (np.float64, 136, 83, 606),        # 6 fp64 edge tiles, S 114, 19 pieces each
+    # 64^2 with two K groups
+    (np.float32, 1145, 1171, 3840),    # 256 + 86, crossing, unaligned ld
+    (np.float32, 135, 3743, 4379),     # 177 tiles, no full round, crossing, K tail 27
+    (np.float32, 5933, 138, 2931),     # 256 + 23, S 253, K tail 19
 ]
 
 
