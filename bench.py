@@ -176,22 +176,43 @@ PROFILES = os.path.join(ROOT, "profiles")
 LIB = os.path.join(ROOT, "precision_gemm_02_amd", "libpgemm.so")
 
 
+def _build_module():
+    """precision_gemm_02_amd/build.py, loaded by path (no library import)."""
+    import importlib.util
+    path = os.path.join(ROOT, "precision_gemm_02_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("_pgemm_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def library_digest() -> str:
-    """sha256 of the built libpgemm.so (the code that runs; the build is
-    deterministic, so a change to comments alone keeps the digest)."""
-    import hashlib
+    """Digest of the kernel sources and build flags (build.source_digest):
+    the same at any build path, so counters recorded from one build apply to
+    another build of the same sources.  "stale" if libpgemm.so is older than
+    a source file (the sources no longer describe the library that runs)."""
     if not os.path.exists(LIB):
         return "unbuilt"
-    return hashlib.sha256(open(LIB, "rb").read()).hexdigest()[:16]
+    b = _build_module()
+    newest = max(os.path.getmtime(os.path.join(b.CSRC, f)) for f in os.listdir(b.CSRC))
+    newest = max(newest, os.path.getmtime(os.path.join(b.INCLUDE, "pgemm.h")))
+    if os.path.getmtime(LIB) + 1.0 < newest:
+        return "stale"
+    return b.source_digest()
+
+
+_warned = set()
 
 
 def recorded_profile(variant: str, workload: str) -> dict:
     """Values measured by rocprofv3 counter runs for this variant and
     workload, as recorded in profiles/*counters*.md, or {} if none matches
-    them and the built library (the kernel changed since they were taken)."""
+    them and the current sources (the kernel changed since they were
+    taken); a warning names what did not match."""
     if not os.path.isdir(PROFILES):
         return {}
     digest = library_digest()
+    seen = []
     for f in sorted(os.listdir(PROFILES)):
         if "counters" not in f:
             continue
@@ -200,9 +221,16 @@ def recorded_profile(variant: str, workload: str) -> dict:
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].strip().split(": ", 1)
                 kv[k.strip("`")] = v.strip().strip("`")
-        if (kv.get("variant") == variant and kv.get("workload") == workload
-                and kv.get("library_digest") == digest):
-            return kv
+        if kv.get("variant") == variant and kv.get("workload") == workload:
+            if kv.get("library_digest") == digest:
+                return kv
+            seen.append((f, kv.get("library_digest")))
+    if (variant, workload) not in _warned:
+        _warned.add((variant, workload))
+        log("no recorded counters for %s on %s with source digest %s%s" % (
+            variant, workload, digest,
+            "" if not seen else " (recorded with other digests: %s)" % ", ".join(
+                "%s in %s" % (d, f) for f, d in seen)))
     return {}
 
 

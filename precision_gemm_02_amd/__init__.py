@@ -125,11 +125,26 @@ def status_string(status: int) -> str:
 
 
 def _addr(x):
-    """Device address of a tensor (its data pointer) or an int; None -> NULL."""
+    """Device address of a tensor (its data pointer) or an int; None -> NULL.
+
+    A tensor must live on the current HIP device: the kernels dereference
+    the address on the GPU, where a host address (a CPU tensor's) or another
+    device's memory would be a memory-access fault, not an error code.  An
+    int is taken as a device address as is."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    dev = getattr(x, "device", None)
+    if dev is None:
+        raise TypeError("expected a torch tensor, an int device address or None, got %s"
+                        % type(x).__name__)
+    if dev.type != "cuda":
+        raise TypeError("tensor is on %s; pgemm needs device (HIP) memory" % dev)
+    import torch
+    if dev.index != torch.cuda.current_device():
+        raise TypeError("tensor is on %s but the current device is cuda:%d"
+                        % (dev, torch.cuda.current_device()))
     return x.data_ptr()
 
 
@@ -260,17 +275,25 @@ def variants():
     return out
 
 
-def _layout(t):
-    """('col', ld) for a column-major 2-D view, ('row', ld) for row-major."""
+def _layouts(t):
+    """{layout: ld} of every layout a 2-D tensor's strides fit: 'col'
+    (element (i, j) at i + j*ld) and/or 'row' (at i*ld + j).  A dimension of
+    size 1 has no stride to speak of, so a column (r x 1) fits column-major
+    with ld = r and row-major with ld = 1 alike; callers take the layout
+    the other operands agree on."""
     if t.dim() != 2:
         raise ValueError("expected a 2-D tensor")
     r, c = t.shape
     s0, s1 = t.stride()
-    if s0 == 1 and (c <= 1 or s1 >= max(1, r)):
-        return "col", max(s1, max(1, r)) if c > 1 else max(1, r)
-    if s1 == 1 and (r <= 1 or s0 >= max(1, c)):
-        return "row", max(s0, max(1, c)) if r > 1 else max(1, c)
-    raise ValueError("tensor with strides %s is neither column- nor row-major" % (t.stride(),))
+    out = {}
+    if (r <= 1 or s0 == 1) and (c <= 1 or s1 >= max(1, r)):
+        out["col"] = s1 if c > 1 else max(1, r)
+    if (c <= 1 or s1 == 1) and (r <= 1 or s0 >= max(1, c)):
+        out["row"] = s0 if r > 1 else max(1, c)
+    if not out:
+        raise ValueError("tensor with strides %s is neither column- nor row-major"
+                         % (t.stride(),))
+    return out
 
 
 def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
@@ -288,12 +311,14 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
     if k2 != k or tuple(C.shape) != (m, n):
         raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
                                                               tuple(C.shape)))
-    la, lb, lc = _layout(A), _layout(B), _layout(C)
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        _addr(t)   # on the current device (TypeError otherwise)
+    la, lb, lc = _layouts(A), _layouts(B), _layouts(C)
     fn = gemm_f32 if A.dtype == torch.float32 else gemm_f64
-    if la[0] == lb[0] == lc[0] == "col":
-        fn(m, n, k, alpha, A, la[1], B, lb[1], beta, C, lc[1], stream)
-    elif la[0] == lb[0] == lc[0] == "row":
-        fn(n, m, k, alpha, B, lb[1], A, la[1], beta, C, lc[1], stream)
+    if "col" in la and "col" in lb and "col" in lc:
+        fn(m, n, k, alpha, A, la["col"], B, lb["col"], beta, C, lc["col"], stream)
+    elif "row" in la and "row" in lb and "row" in lc:
+        fn(n, m, k, alpha, B, lb["row"], A, la["row"], beta, C, lc["row"], stream)
     else:
         raise ValueError("A, B and C must share one layout")
     return C

@@ -32,6 +32,25 @@ CFLAGS = [
 ]
 
 
+def source_digest(extra_flags=()) -> str:
+    """sha256 (first 16 hex digits) of what determines the built kernels: the
+    compiler flags and the bytes of every file under csrc/ and of the public
+    header.  Unlike a hash of libpgemm.so it does not depend on the directory
+    the library is built in (hipcc derives per-file symbols from the path)."""
+    import hashlib
+    h = hashlib.sha256()
+    h.update(" ".join([ARCH, *[f for f in CFLAGS if not f.startswith("-I")],
+                       *extra_flags]).encode())
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC))
+    files.append(os.path.join(INCLUDE, "pgemm.h"))
+    for path in files:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]

@@ -321,3 +321,69 @@ def test_matmat_host_workspace_size():
         assert pg.matmat_host_workspace(lda, ldb, ldc, n1, n2, n3) == want
     assert pg.matmat_host_workspace(5, 5, 5, 0, 5, 5) == 0
     assert pg.matmat_host_workspace(4, 5, 5, 5, 5, 5) == 0    # lda < N2
+
+
+def test_cpu_tensors_are_refused_before_any_call(monkeypatch):
+    """A CPU tensor's data pointer is a host address: handed to a kernel it
+    would fault the GPU.  The binding refuses it with TypeError before the
+    library is called (the library is replaced by one that records calls)."""
+    import torch
+    calls = []
+
+    class Rec:
+        def __getattr__(self, name):
+            def f(*a):
+                calls.append(name)
+                return 0
+            return f
+
+    monkeypatch.setattr(pg, "_lib", Rec())
+    A = torch.zeros(8, 8)
+    B = torch.zeros(8, 8)
+    C = torch.zeros(8, 8)
+    with pytest.raises(TypeError):
+        pg.gemm_f32(8, 8, 8, 1.0, A, 8, B, 8, 0.0, C, 8, stream=0)
+    with pytest.raises(TypeError):
+        pg.gemm_f64(8, 8, 8, 1.0, A.double(), 8, B.double(), 8, 0.0, C.double(), 8, stream=0)
+    with pytest.raises(TypeError):
+        pg.matmat_f64(8, 8, 8, A.double(), B.double(), C.double(), 8, 8, 8, stream=0)
+    with pytest.raises(TypeError):
+        pg.gemm_f32_ws(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8,
+                       torch.zeros(16, dtype=torch.uint8), 16, stream=0)
+    with pytest.raises(TypeError):
+        pg.gemm(A, B, C)
+    with pytest.raises(TypeError):
+        pg.gemm_f32(8, 8, 8, 1.0, "not a pointer", 8, FAKE, 8, 0.0, FAKE, 8, stream=0)
+    assert calls == []
+    # integer device addresses pass through unchanged (the caller vouches)
+    pg.gemm_f32(8, 8, 8, 1.0, FAKE, 8, FAKE, 8, 0.0, FAKE, 8, stream=0)
+    assert calls == ["gemm_f32"]
+
+
+def test_layouts_of_vectors_fit_both():
+    """_layouts: a dimension of size 1 fits column- and row-major alike, so
+    matrix-vector and outer products of contiguous (row-major) or
+    column-major tensors find one common layout."""
+    import torch
+    L_ = pg._layouts
+    # contiguous (row-major) A (m x k), B (k x 1), C (m x 1): n == 1
+    assert L_(torch.empty(5, 3)) == {"row": 3}
+    assert L_(torch.empty(3, 1)) == {"col": 3, "row": 1}
+    # k == 1: A (m x 1), B (1 x n)
+    assert L_(torch.empty(1, 4)) == {"col": 1, "row": 4}
+    # column-major views
+    assert L_(torch.empty(3, 5).t()) == {"col": 5}
+    assert L_(torch.empty(1, 5).t()) == {"col": 5, "row": 1}
+    # padded column-major: ld from the stride
+    assert L_(torch.empty(4, 10).t()[:7, :]) == {"col": 10}
+    assert L_(torch.empty(1, 1)) == {"col": 1, "row": 1}
+    with pytest.raises(ValueError):
+        L_(torch.empty(4, 6)[:, ::2])
+    with pytest.raises(ValueError):
+        L_(torch.empty(2, 3, 4))
+    # every combination of a matrix-vector call shares a layout
+    for (m, k, n) in ((5, 3, 1), (5, 1, 4), (1, 3, 4), (1, 1, 1)):
+        la, lb, lc = L_(torch.empty(m, k)), L_(torch.empty(k, n)), L_(torch.empty(m, n))
+        assert "row" in la and "row" in lb and "row" in lc
+        la, lb, lc = (L_(torch.empty(c, r).t()) for (r, c) in ((m, k), (k, n), (m, n)))
+        assert "col" in la and "col" in lb and "col" in lc
