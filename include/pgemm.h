@@ -20,9 +20,10 @@
  * Memory.  A, B, C are DEVICE pointers on the current HIP device, owned by
  *   the caller (matmat_f64_host alone takes host pointers).  The library
  *   allocates nothing per call and keeps no state besides read-only kernel
- *   code and a per-device compute-unit count; scratch memory, where an entry
- *   point uses any, is a caller workspace.  C must not overlap A or B; A may
- *   equal B.
+ *   code, a per-device compute-unit count and, for gemm_f32_noalloc alone, a
+ *   fixed scratch array per device; the scratch memory of every other entry
+ *   point that uses any is a caller workspace.  C must not overlap A or B; A
+ *   may equal B.
  * Stream.  `stream` is a hipStream_t passed as void*; NULL means the default
  *   stream.  Every call is stream-ordered and asynchronous: it returns after
  *   enqueueing work; the caller synchronizes (matmat_f64_host alone returns
@@ -53,6 +54,10 @@ extern "C" {
 #define PGEMM_OK 0
 #define PGEMM_EHIP (-100)      /* a HIP launch, copy or synchronization failed */
 #define PGEMM_EVARIANT (-101)  /* unknown kernel variant id */
+#define PGEMM_ESCRATCH (-102)  /* the shape needs more than PGEMM_SCRATCH_BYTES of scratch */
+
+/* Size of the library-owned scratch array of gemm_f32_noalloc, per device. */
+#define PGEMM_SCRATCH_BYTES (32u << 20)
 
 /*
  * Single precision.  C(m x n) <- alpha * A(m x k) * B(k x n) + beta * C.
@@ -135,6 +140,34 @@ int gemm_f64_ws(int m, int n, int k, double alpha, const double *A, int lda,
                 void *workspace, size_t workspace_bytes, void *stream);
 size_t pgemm_workspace_f32(int m, int n, int k);
 size_t pgemm_workspace_f64(int m, int n, int k);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * contract and same result bits as gemm_f32_ws given a workspace of
+ * pgemm_workspace_f32(m, n, k) bytes, but the stream-K partial sums go to a
+ * scratch array that the library itself holds in device memory: a
+ * file-scope array of PGEMM_SCRATCH_BYTES (32 MiB) per device, reserved
+ * when the library's code is loaded on that device and kept until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the caller passes A, B and C as for
+ * gemm_f32.
+ *
+ *   returns PGEMM_ESCRATCH, before any launch, if the shape's stream-K
+ *   workspace would exceed PGEMM_SCRATCH_BYTES (it never does on a device of
+ *   up to 256 compute units: the largest plan there is 2 x 256 tiles of
+ *   128 x 128 fp32 partial sums, exactly 32 MiB); PGEMM_EHIP if the array's
+ *   device address cannot be obtained.
+ *
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents; no part of it needs to start at zero (each partial sum is
+ * written before the fix-up kernel reads it).  Calls on one device must
+ * therefore be ordered (e.g. issued on one stream): two calls that overlap
+ * on one device race on the array and may return wrong results.
+ */
+int gemm_f32_noalloc(int m, int n, int k, float alpha, const float *A, int lda,
+                     const float *B, int ldb, float beta, float *C, int ldc,
+                     void *stream);
 
 /*
  * The lecture's matmat on HOST memory ("HPC - Lecture 13 - MatMat GPU",

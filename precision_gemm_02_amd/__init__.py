@@ -62,7 +62,7 @@ _EXPORTS = ("gemm_f32", "gemm_f64", "matmat_f64", "pgemm_status_string",
             "pgemm_num_variants", "gemm_f32_variant", "gemm_f64_variant",
             "gemm_f32_ws", "gemm_f64_ws", "pgemm_workspace_f32", "pgemm_workspace_f64",
             "matmat_f64_host", "pgemm_matmat_host_workspace", "pgemm_select_ws_f32",
-            "pgemm_select_ws_f64", "pgemm_device_info")
+            "pgemm_select_ws_f64", "pgemm_device_info", "gemm_f32_noalloc")
 _missing = [n for n in _EXPORTS if not hasattr(_lib, n)]
 if _missing:
     raise ImportError("libpgemm.so is older than this binding (no %s); rebuild it with "
@@ -82,6 +82,7 @@ _lib.pgemm_select_ws_f32.argtypes = _lib.pgemm_select_f32.argtypes + [_sz, ctype
 _lib.pgemm_select_ws_f64.argtypes = _lib.pgemm_select_f64.argtypes + [_sz, ctypes.POINTER(_i),
                                                                        ctypes.POINTER(_i)]
 _lib.gemm_f32_ws.argtypes = _lib.gemm_f32.argtypes[:11] + [_vp, _sz, _vp]
+_lib.gemm_f32_noalloc.argtypes = _lib.gemm_f32.argtypes
 _lib.gemm_f64_ws.argtypes = _lib.gemm_f64.argtypes[:11] + [_vp, _sz, _vp]
 _lib.pgemm_workspace_f32.argtypes = [_i, _i, _i]
 _lib.pgemm_workspace_f64.argtypes = [_i, _i, _i]
@@ -98,13 +99,15 @@ _lib.pgemm_variant_name.restype = ctypes.c_char_p
 for _name in ("gemm_f32", "gemm_f64", "matmat_f64", "gemm_f32_variant", "gemm_f64_variant",
               "pgemm_select_f32", "pgemm_select_f64", "pgemm_num_variants", "gemm_f32_ws",
               "gemm_f64_ws", "pgemm_select_ws_f32", "pgemm_select_ws_f64",
-              "pgemm_device_info"):
+              "pgemm_device_info", "gemm_f32_noalloc"):
     getattr(_lib, _name).restype = _i
 _lib.pgemm_device_info.argtypes = [ctypes.POINTER(_i), ctypes.POINTER(_i)]
 
 PGEMM_OK = 0
 PGEMM_EHIP = -100
 PGEMM_EVARIANT = -101
+PGEMM_ESCRATCH = -102
+PGEMM_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = _EXPORTS
 
@@ -190,6 +193,13 @@ def gemm_f64_ws(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws, ws_bytes, stre
     """gemm_f64 with a device workspace for balancing leftover tiles."""
     _check(_lib.gemm_f64_ws(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta, _addr(C), ldc,
                             _addr(ws), ws_bytes, _stream(stream)), "gemm_f64_ws")
+
+
+def gemm_f32_noalloc(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """gemm_f32_ws on the library's own fixed scratch array (allocates
+    nothing; calls on one device must be ordered)."""
+    _check(_lib.gemm_f32_noalloc(m, n, k, alpha, _addr(A), lda, _addr(B), ldb, beta,
+                                 _addr(C), ldc, _stream(stream)), "gemm_f32_noalloc")
 
 
 def workspace_f32(m, n, k) -> int:

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "pgemm.h"
 #include "variants.hpp"
@@ -480,6 +481,28 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
              static_cast<T*>(ws), strip, s);
 }
 
+// The scratch array of gemm_f32_noalloc: one copy per device, at its own
+// address on each.  In host code `scratch` is only a stand-in for the
+// device symbol; its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept per device below.
+static __device__ __align__(256) unsigned char scratch[PGEMM_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device (nullptr if HIP cannot
+// give it).
+void* scratch_address() {
+  static std::mutex mu;
+  static void* ptrs[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 // Workspace the stream-K path would use for this shape (0: none).
 template <typename T>
 size_t workspace_impl(int m, int n, int k) {
@@ -536,6 +559,21 @@ int gemm_f64_ws(int m, int n, int k, double alpha, const double* A, int lda,
                 size_t workspace_bytes, void* stream) {
   return gemm_impl<double>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
                            workspace_bytes, stream);
+}
+
+// gemm_f32_ws on the library's scratch array.  Any workspace of at least
+// the shape's own need gives gemm_f32_ws the same plan, so passing the
+// array's full size reproduces gemm_f32_ws with pgemm_workspace_f32 bytes.
+int gemm_f32_noalloc(int m, int n, int k, float alpha, const float* A, int lda,
+                     const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
+  const int st = check_args(m, n, k, alpha, A, lda, B, ldb, C, ldc);
+  if (st != 0) return st;
+  if (m == 0 || n == 0) return PGEMM_OK;
+  if (workspace_impl<float>(m, n, k) > PGEMM_SCRATCH_BYTES) return PGEMM_ESCRATCH;
+  void* ws = scratch_address();
+  if (ws == nullptr) return PGEMM_EHIP;
+  return gemm_impl<float>(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws,
+                          PGEMM_SCRATCH_BYTES, stream);
 }
 
 size_t pgemm_workspace_f32(int m, int n, int k) { return workspace_impl<float>(m, n, k); }
@@ -624,6 +662,9 @@ const char* pgemm_status_string(int status) {
     case PGEMM_OK: return "success";
     case PGEMM_EHIP: return "HIP call failed (kernel launch, copy or synchronization)";
     case PGEMM_EVARIANT: return "unknown or inapplicable kernel variant";
+    case PGEMM_ESCRATCH:
+      return "the shape needs more stream-K scratch than the library's fixed array "
+             "(PGEMM_SCRATCH_BYTES); call gemm_f32_ws with a workspace instead";
     default: break;
   }
   if (status < 0 && status >= -14) return "invalid argument (see the argument position)";

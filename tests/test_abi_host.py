@@ -387,3 +387,29 @@ def test_layouts_of_vectors_fit_both():
         assert "row" in la and "row" in lb and "row" in lc
         la, lb, lc = (L_(torch.empty(c, r).t()) for (r, c) in ((m, k), (k, n), (m, n)))
         assert "col" in la and "col" in lb and "col" in lc
+
+
+def test_noalloc_host_checks_and_scratch_bound():
+    """gemm_f32_noalloc: argument codes in gemm_f32's positions and quick
+    returns before any HIP call; the scratch size the header states is the
+    binding's; and on 256 compute units (the MI355X, and the fallback without
+    a GPU) no fp32 shape's stream-K workspace exceeds it, so the call never
+    returns PGEMM_ESCRATCH there."""
+    nf = L.gemm_f32_noalloc
+    assert nf(4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4, None) == -6
+    assert nf(4, 4, 4, 1.0, None, 4, FAKE, 4, 0.0, FAKE, 4, None) == -5
+    assert nf(-1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4, None) == -1
+    assert nf(0, 5, 5, 1.0, None, 1, None, 5, 1.0, None, 1, None) == 0
+    hdr = open(HEADER).read()
+    m = re.search(r"#define PGEMM_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and (int(m.group(1)) << int(m.group(2))) == pg.PGEMM_SCRATCH_BYTES
+    assert "scratch" in pg.status_string(pg.PGEMM_ESCRATCH)
+    rng = np.random.default_rng(11)
+    worst = 0
+    for _ in range(3000):
+        m_, n_ = (int(x) for x in rng.integers(1, 12000, 2))
+        k_ = int(rng.integers(1, 9000))
+        worst = max(worst, pg.workspace_f32(m_, n_, k_))
+    assert 0 < worst <= pg.PGEMM_SCRATCH_BYTES
+    # the largest plan: 256 stream-K workgroups of 128 x 128 tiles
+    assert pg.workspace_f32(3840, 3840, 3840) == pg.PGEMM_SCRATCH_BYTES
