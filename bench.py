@@ -3,22 +3,24 @@
 One step = one call C <- alpha*A*B + beta*C through the C ABI on inputs that
 are already resident in HBM: gemm_f32 / gemm_f64, or gemm_*_ws with the
 workspace the library asks for when the tiles of C leave a partly filled last
-round (the 4097x3001x1023 workload), or matmat_f64 for the row-major fp64
-workload.  W untimed warmup steps, then K timed steps back to back,
-bracketed by torch.cuda.synchronize(); then, outside the timed region, K more
-launches each bracketed by HIP events on the stream they are launched on,
-which give the kernel's own average duration for the roofline figure.
+round, or matmat_f64 for the row-major fp64 workload.  W untimed warmup
+steps (continued for at least --min-warmup-seconds), then exactly K timed
+steps back to back, bracketed by torch.cuda.synchronize() and, on the launch
+stream, by two HIP events.
 
 Prints ONE JSON line.  ``value`` is the whole-job throughput in TFLOPS
-(2*M*N*K per step / wall time per step).  ``roofline`` compares the GEMM
-kernel's event-timed throughput with MI355X's dense fp32 (or fp64) matrix
-peak.  ``cpu_baseline`` times the CPU oracle (test infrastructure, built
-from oracle/oracle.c) on a bounded sample of the same workload: the first J
-columns of C, with J chosen for roughly 10-20 s of CPU work; the same sample
-also checks the GPU's first output against the oracle.
+(2*M*N*K per step / wall time per step).  ``roofline`` compares the
+throughput the two events measure (the stream's GPU time for the K steps)
+with MI355X's dense fp32 (or fp64) matrix peak.  ``secondary`` holds one such
+line for every other configuration point (steps scaled up for short kernels:
+about 50 ms of GPU time each).  ``cpu_baseline`` times the CPU oracle (test
+infrastructure, built from oracle/oracle.c) on a bounded sample of the
+primary workload: the first J columns of C, with J chosen for roughly 10-20 s
+of CPU work; the same sample also checks the GPU's first output against the
+oracle.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--secondary NAME ...]
+                       [--no-cpu-baseline] [--secondary NAME ...] [--sweep]
 """
 from __future__ import annotations
 
@@ -51,8 +53,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="sgemm_sweep_8192")
     ap.add_argument("--secondary", nargs="*",
-                    default=["sgemm_2048", "sgemm_ragged", "dgemm_rowmajor",
-                             "sgemm_shard_8192_g8"])
+                    default=["sgemm_2048", "sgemm_128", "sgemm_sweep_512", "sgemm_sweep_1024",
+                             "sgemm_sweep_2048", "sgemm_sweep_4096", "sgemm_ragged",
+                             "dgemm_rowmajor", "sgemm_shard_8192_g8"],
+                    help="workloads timed after the primary one, each on its own line "
+                         "(default: every configuration point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--min-warmup-seconds", type=float, default=0.3,
@@ -109,18 +114,26 @@ class Resident:
         vid, self.sk_wgs, self.strip_rows = sel(*self.args, self.ws_bytes)
         self.variant = pg.variants().get(vid, "none")
 
-    def launch(self):
-        if self.p.rowmajor:
-            p = self.p
-            self.pg.matmat_f64(p.lda, p.ldb, p.ldc, self.A.data_ptr(), self.B.data_ptr(),
-                               self.C.data_ptr(), p.m, p.k, p.n, self.stream)
+        # One C-ABI call per step, its arguments converted once here: the
+        # launch loop of a microsecond kernel must not be paced by Python.
+        lib, sh = pg.library(), self.stream.cuda_stream
+        if p.rowmajor:
+            fn = lib.matmat_f64
+            cargs = (p.lda, p.ldb, p.ldc, self.A.data_ptr(), self.B.data_ptr(),
+                     self.C.data_ptr(), p.m, p.k, p.n, sh)
         elif self.ws_bytes:
-            fn = self.pg.gemm_f32_ws if self.dt == "f32" else self.pg.gemm_f64_ws
-            fn(*self.args, self.ws.data_ptr(), self.ws_bytes, stream=self.stream)
-        elif self.dt == "f32":
-            self.pg.gemm_f32(*self.args, stream=self.stream)
+            fn = lib.gemm_f32_ws if self.dt == "f32" else lib.gemm_f64_ws
+            cargs = (*self.args, self.ws.data_ptr(), self.ws_bytes, sh)
         else:
-            self.pg.gemm_f64(*self.args, stream=self.stream)
+            fn = lib.gemm_f32 if self.dt == "f32" else lib.gemm_f64
+            cargs = (*self.args, sh)
+        self._fn, self._cargs = fn, cargs
+
+    def launch(self):
+        st = self._fn(*self._cargs)
+        if st != 0:
+            raise RuntimeError("%s: status %d (%s)" % (self.entry, st,
+                                                      self.pg.status_string(st)))
 
     def reset_c(self):
         if self.p.beta != 0:
@@ -132,44 +145,70 @@ class Resident:
         return s * (p.m * p.k + p.k * p.n + p.m * p.n * (1 + (p.beta != 0)))
 
 
-def time_workload(r: Resident, steps: int, warmup: int, min_warm_s: float):
-    """W warmup launches, continued until at least ``min_warm_s`` of wall time
+def warm_up(r: Resident, warmup: int, min_warm_s: float):
+    """At least ``warmup`` launches, continued until ``min_warm_s`` of wall time
     has passed (the GPU raises its clock over a few hundred ms of sustained
     load; a short kernel timed right after an idle gap measures the ramp, not
-    the kernel).  Then the timed region: exactly ``steps`` launches back to
-    back between two synchronizations (wall clock, nothing else on the
-    stream).  Then, outside it, the same number of launches each between two
-    HIP events on the launch stream, for the kernel's own time.  Returns
-    (wall ms per step, per-launch kernel ms, warmup launches)."""
+    the kernel).  C is restored every 64 launches (|beta| > 1 grows it).
+    Returns (launches, wall seconds per launch over the last batch)."""
     import torch
     n_warm = 0
     t_end = time.perf_counter() + min_warm_s
+    t_batch, n_batch = time.perf_counter(), 0
+    per = None
     while n_warm < warmup or time.perf_counter() < t_end:
         r.launch()
         n_warm += 1
+        n_batch += 1
         if n_warm % 8 == 0:
             torch.cuda.synchronize()
+            now = time.perf_counter()
+            per = (now - t_batch) / n_batch
+            t_batch, n_batch = now, 0
         if n_warm % 64 == 0:
-            r.reset_c()   # beta != 0: keep C finite (|beta| > 1 grows it each call)
+            r.reset_c()
+    torch.cuda.synchronize()
+    if per is None:
+        per = (time.perf_counter() - t_batch) / max(n_batch, 1)
     r.reset_c()
+    torch.cuda.synchronize()
+    return n_warm, per
+
+
+def timed_steps(r: Resident, steps: int):
+    """The timed region: exactly ``steps`` launches back to back between two
+    synchronizations, with a HIP event recorded on the launch stream right
+    before the first launch and right after the last.  Returns (wall ms per
+    step, GPU ms per step from the two events).  The events see the stream's
+    own time for the steps (every kernel a step launches, and the gaps
+    between launches), not the host's."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(r.stream)
     for _ in range(steps):
         r.launch()
+    e1.record(r.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
     r.reset_c()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     torch.cuda.synchronize()
-    for s, e in ev:
-        s.record(r.stream)
-        r.launch()
-        e.record(r.stream)
-    torch.cuda.synchronize()
-    kern_ms = [s.elapsed_time(e) for s, e in ev]
-    r.reset_c()
-    return wall / steps * 1e3, kern_ms, n_warm
+    return wall / steps * 1e3, gpu_ms / steps
+
+
+def auto_steps(r: Resident, base: int, per_launch_s: float, region_s: float = 0.05) -> int:
+    """Steps for a secondary workload: at least ``base``, and enough for about
+    ``region_s`` of GPU time (microsecond kernels need thousands of steps for
+    a stable average), at most 20000; at most 300 when |beta| > 1, so that C
+    stays finite."""
+    n = max(base, int(region_s / max(per_launch_s, 1e-7)))
+    n = min(n, 20000)
+    if abs(r.p.beta) > 1:
+        n = min(n, 300)
+    return n
 
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -262,13 +301,16 @@ def device_peak(dt: str):
     return cus * khz * 1e3 * per_cycle / 1e12, cus, khz / 1e3
 
 
-def roofline(r: Resident, kern_ms: list):
-    """Matrix-core roofline of the GEMM kernel: achieved flops per launch over
-    the mean of the per-launch event times (the median and the minimum are
-    reported beside it).  `peak` is the published one; the peak recomputed
-    from the device's properties is given beside it."""
-    kern_ms_mean = float(np.mean(kern_ms))
-    achieved = r.flops / (kern_ms_mean * 1e-3) / 1e12
+def roofline(r: Resident, gpu_ms: float):
+    """Matrix-core roofline of the step: algorithmic flops per step (2MNK)
+    over the GPU time per step that two HIP events around the timed region
+    measured on the launch stream.  A step is one library call: the GEMM
+    kernel plus, where the shape needs them, the strip kernel or the
+    stream-K fix-up kernel, which this time includes.  `peak` is the
+    published one; the peak recomputed from the device's properties is given
+    beside it.  The largest problems are bound by the matrix cores; the
+    smallest (128^3) by launch latency, and its time is also given in us."""
+    achieved = r.flops / (gpu_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[r.dt]
     dpeak, cus, mhz = device_peak(r.dt)
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
@@ -278,9 +320,9 @@ def roofline(r: Resident, kern_ms: list):
             "traffic": recorded_traffic(r.variant, r.name),
             "counters": recorded_counters(r.variant, r.name),
             "algorithmic_bytes": r.algorithmic_bytes(),
-            "kernel": r.variant, "stream_k_wgs": r.sk_wgs, "strip_rows": r.strip_rows, "kernel_ms_mean": round(kern_ms_mean, 4),
-            "kernel_ms_median": round(float(np.median(kern_ms)), 4),
-            "kernel_ms_min": round(float(np.min(kern_ms)), 4),
+            "kernel": r.variant, "stream_k_wgs": r.sk_wgs, "strip_rows": r.strip_rows,
+            "kernel_ms_mean": round(gpu_ms, 5), "kernel_us_mean": round(gpu_ms * 1e3, 2),
+            "timing": "HIP events on the launch stream around the timed region, per step",
             "entry": r.entry, "workspace_bytes": r.ws_bytes,
             "library_digest": library_digest()}
 
@@ -344,8 +386,8 @@ def sweep(args):
             out = r.C.cpu().numpy()
             got = gi.logical_colmajor(out, p.m, p.n, p.ldc).astype(np.float64)
         r.reset_c()
-        _, kern_ms, _ = time_workload(r, max(args.steps, 10), args.warmup,
-                                          args.min_warmup_seconds)
+        _, per = warm_up(r, args.warmup, args.min_warmup_seconds)
+        _, kern_med = timed_steps(r, auto_steps(r, max(args.steps, 10), per))
         cold_ms = cold_kernel_ms(r, flush, 5)
         cols = p.n if p.m * p.n * p.k <= 4096 ** 3 else 512
         t0 = time.perf_counter()
@@ -370,7 +412,6 @@ def sweep(args):
         else:
             ok = rel <= 1e-12
         cnt = recorded_counters(r.variant, r.name)
-        kern_med = float(np.median(kern_ms))
         tflops = r.flops / (kern_med * 1e-3) / 1e12
         rows.append((name, "%dx%dx%d" % (p.m, p.n, p.k), r.entry, r.variant, kern_med, tflops,
                      100 * tflops / PEAK_TFLOPS[r.dt], cnt, maxabs, rel, ok, t_or, cols, p.n,
@@ -378,7 +419,7 @@ def sweep(args):
                      100 * tflops / device_peak(r.dt)[0]))
         del r
         torch.cuda.empty_cache()
-    print("| workload | M×N×K | entry, variant | kernel ms (median) | TFLOP/s | %% of peak "
+    print("| workload | M×N×K | entry, variant | GPU ms per call | TFLOP/s | %% of peak "
           "(device props) | cold-cache ms | MfmaUtil | LDS bank conflicts | max\\|ΔC\\| "
           "| rel. Frobenius | parity | oracle s (%d threads) | oracle GFLOP/s |" % cores)
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
@@ -450,12 +491,11 @@ def main():
         p = r.p
         first_out = r.C[: p.ldc * p.n].view(p.n, p.ldc)[:, : p.m].t().cpu().numpy()
     r.reset_c()
-    ms_step, kern_ms, n_warm = time_workload(r, args.steps, args.warmup,
-                                             args.min_warmup_seconds)
+    n_warm, _ = warm_up(r, args.warmup, args.min_warmup_seconds)
+    ms_step, gpu_ms = timed_steps(r, args.steps)
     value = r.flops / (ms_step * 1e-3) / 1e12
-    log("%s: %.3f ms/step, kernel mean %.3f ms -> %.2f TFLOPS" % (r.name, ms_step,
-                                                                   float(np.mean(kern_ms)),
-                                                                   value))
+    log("%s: %.3f ms/step wall, %.3f ms/step GPU -> %.2f TFLOPS" % (r.name, ms_step, gpu_ms,
+                                                                    value))
     p = r.p
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1,
@@ -468,7 +508,7 @@ def main():
                    "layout": "row-major (operand swap)" if p.rowmajor else "column-major",
                    "variant": r.variant, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / PEAK_TFLOPS[r.dt], 2),
-        "roofline": roofline(r, kern_ms),
+        "roofline": roofline(r, gpu_ms),
     }
     main_problem = r.p
     secondary = []
@@ -478,16 +518,17 @@ def main():
         del r
         torch.cuda.empty_cache()
         r2 = Resident(name)
-        steps2 = max(args.steps, 20)
-        ms2, km2, nw2 = time_workload(r2, steps2, args.warmup, args.min_warmup_seconds)
+        nw2, per = warm_up(r2, args.warmup, args.min_warmup_seconds)
+        steps2 = auto_steps(r2, max(args.steps, 20), per)
+        ms2, g2 = timed_steps(r2, steps2)
         v2 = r2.flops / (ms2 * 1e-3) / 1e12
-        log("%s: %.3f ms/step, kernel mean %.3f ms -> %.2f TFLOPS" % (name, ms2,
-                                                                       float(np.mean(km2)), v2))
+        log("%s: %.4f ms/step wall, %.4f ms/step GPU (%d steps) -> %.2f TFLOPS" % (
+            name, ms2, g2, steps2, v2))
         secondary.append({"workload": name, "value": round(v2, 3), "unit": "TFLOPS",
-                          "ms_per_step": round(ms2, 4), "steps": steps2,
-                          "warmup_launches": nw2, "dtype": r2.dt,
+                          "ms_per_step": round(ms2, 5), "us_per_step": round(ms2 * 1e3, 2),
+                          "steps": steps2, "warmup_launches": nw2, "dtype": r2.dt,
                           "pct_of_peak": round(100 * v2 / PEAK_TFLOPS[r2.dt], 2),
-                          "roofline": roofline(r2, km2)})
+                          "roofline": roofline(r2, g2)})
         r = r2
     if secondary:
         out["secondary"] = secondary

@@ -285,25 +285,33 @@ int strip_rows(const Variant<T>& v, int m) {
   return (r > 0 && r <= kStripRows && m > v.bm) ? r : 0;
 }
 
-// Estimated time of strip_rows_kernel on r rows (same units as estimate): a
-// launch behind the GEMM kernel (~4 us) plus the largest of: its latency
-// chain (~2.5 us per batch of four steps of every thread, ~2 us for the
-// sums), reading B once from HBM (~4 TB/s), every workgroup's reads of the
-// strip of A from the caches (one 128-byte line per inner index, ~7 TB/s:
-// fitted to 8193 x 8192 x 8192, where they dominate), and its multiply-adds
-// on the vector units (~40 TFLOP/s fp32, ~20 fp64).
+// Estimated time of the strip of r rows (same units as estimate): the
+// largest of its latency chain (~2.5 us per batch of four steps of every
+// thread, ~2 us for the sums), reading B once from HBM (~4 TB/s), every
+// workgroup's reads of the strip of A from the caches (one 128-byte line per
+// inner index, ~7 TB/s; `wg_cols` columns per workgroup) and its
+// multiply-adds on the vector units (~40 TFLOP/s fp32, ~20 fp64), plus ~4 us
+// for a launch behind the GEMM kernel when it is a kernel of its own.  Run
+// by extra workgroups of the GEMM's own grid (Variant::fstrip) it has no
+// launch, and it runs beside the last round of tiles, but its loads compete
+// with theirs: on 24 shapes and every class the measured cost (time with the
+// strip minus time of the tiles alone) was 0.2 to 2.8 times the largest term,
+// mostly 1 to 2.  Doubling the estimate changed the choice on 41 of 6000
+// random shapes and lost 1.7 % on them (geometric mean; up to 26 % where a
+// short strip was then avoided, against at most 5.5 % gained), so it is not
+// doubled.
 template <typename T>
-double strip_time(int r, int n, int k) {
+double strip_time(int r, int n, int k, int wg_cols, bool fused) {
   const double s = sizeof(T);
   const double lat = 2.5e-6 * (double)ceil_div(k, 4 * kStripThreads) + 2e-6;
   const double b_s = (double)k * n * s / 4e12;
-  const double a_s = (double)ceil_div(n, kStripCols) * (double)k * 128.0 / 7e12;
+  const double a_s = (double)ceil_div(n, wg_cols) * (double)k * 128.0 / 7e12;
   const double f_s = 2.0 * r * (double)n * k / (sizeof(T) == 4 ? 40e12 : 20e12);
   double t = lat;
   if (b_s > t) t = b_s;
   if (a_s > t) t = a_s;
   if (f_s > t) t = f_s;
-  return (4e-6 + t) / unit_seconds<T>();
+  return ((fused ? 0.0 : 4e-6) + t) / unit_seconds<T>();
 }
 
 // What a call launches: the tile class, its stream-K plan (wgs == 0: none)
@@ -357,7 +365,9 @@ Choice choose(int m, int n, int k, bool sk_ok) {
         }
       }
       if (strip > 0) {
-        e += strip_time<T>(strip, n, k);
+        int sc, cgw;
+        v.strip_shape(strip, n, cus, &sc, &cgw);
+        e += strip_time<T>(strip, n, k, sc * cgw, v.fstrip);
         if (e * 1.02 >= e_cls) continue;
       }
       e_cls = e;
@@ -429,14 +439,19 @@ int run(const Variant<T>& v, int m, int n, int k, T alpha, const T* A, int lda, 
   g.ldb = ldb;
   g.ldc = ldc;
   g.group_m = 4;
-  if (v.launch(g, s) != hipSuccess) return PGEMM_EHIP;
+  int sc = 0;
   if (strip > 0) {
+    v.strip_shape(strip, n, device_cus(), &sc, &g.strip_cgw);
+    if (v.fstrip) g.strip_rows = strip;   // extra workgroups of the same grid
+  }
+  if (v.launch(g, s) != hipSuccess) return PGEMM_EHIP;
+  if (strip > 0 && !v.fstrip) {
     g.M = m;
     int i0 = m - strip;
     void* args[] = {&g, &i0};
     if (hipLaunchKernel(reinterpret_cast<const void*>(&strip_rows_kernel<T>),
-                        dim3((unsigned)ceil_div(n, kStripCols)), dim3(kStripThreads), args, 0,
-                        s) !=
+                        dim3((unsigned)ceil_div(n, (long long)sc * g.strip_cgw)),
+                        dim3(kStripThreads), args, 0, s) !=
         hipSuccess)
       return PGEMM_EHIP;
   }

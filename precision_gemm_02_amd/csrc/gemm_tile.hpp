@@ -113,6 +113,12 @@ struct GemmArgs {
   // row/column fits a signed 32-bit byte count (see buffer_offsets_fit);
   // otherwise all tiles take the masked loads, with 64-bit addresses.
   int buf32;
+  // Rows [M, M + strip_rows) of C below the tiles, computed by strip_wgs
+  // more workgroups at the end of the grid (strip_rows_wg), in kernels
+  // compiled with that role (STRIPF); 0 otherwise.
+  int strip_rows;
+  int strip_wgs;
+  int strip_cgw;   // column groups per strip workgroup (strip_groups)
 };
 
 // Workgroup id -> linear tile id, for `count` workgroups.  The dispatcher
@@ -190,6 +196,32 @@ struct TileCfg {
   // LDS address arithmetic) when that leaves room for the addresses it keeps
   // live; larger tiles would spill.
   static constexpr bool UNROLL = ACC_REGS + 2 * OPS_REGS + STAGE_REGS <= 192;
+  // With beta != 0, the old C of a whole tile can be loaded into registers
+  // during the last K tiles (one 16-byte chunk per lane and K tile) instead
+  // of in the epilogue, when that costs at most 32 registers: the staged
+  // epilogue's chunks (MB columns x WM rows per column block, WM/V chunks
+  // per column) of the CB column blocks, NPF_C chunks per lane.
+  static constexpr int EPI_CPC = WM / V;
+  static constexpr int EPI_NI = STAGED_EPI ? TR::MB * EPI_CPC / 64 : 1;
+  static constexpr int NPF_C = CB * EPI_NI;
+  static constexpr bool PF_C =
+      STAGED_EPI && KS == 1 && UNROLL && STAGES > 2 && NPF_C * V * (int)sizeof(T) / 4 <= 32;
+  // K tiles over which those loads are spread: whole trips of the unrolled
+  // steady state
+  static constexpr int PF_ITERS = (NPF_C + STAGES - 1) / STAGES * STAGES;
+  // When the grid also computes strip rows (one K group per strip
+  // workgroup: its latency passes beside the tiles), the strip role's sums
+  // per thread (at most STRIP_ACC elements, STRIP_SCMAX columns per wave)
+  // must not take more registers than the tile role, or fewer tiles would
+  // share a compute unit.
+  // Waves per SIMD that the LDS allows (160 KiB per compute unit, NT/256
+  // waves per SIMD per workgroup): the kernels with a strip role ask the
+  // compiler to keep that occupancy.
+  static constexpr int LDS_OCC = (160 * 1024 / LDS_BYTES) * (NT / 256) > 8
+                                     ? 8
+                                     : (160 * 1024 / LDS_BYTES) * (NT / 256);
+  static constexpr int STRIP_SCMAX = (sizeof(T) == 4 && BM >= 128) ? 8 : (sizeof(T) == 4 ? 4 : 2);
+  static constexpr int STRIP_ACC = (sizeof(T) == 4 && BM >= 128) ? 16 : (sizeof(T) == 4 ? 8 : 4);
   static_assert(WM * WGM == BM && WN * WGN == BN, "waves tile the block");
   static_assert(RB * TR::MB == WM && CB * TR::MB == WN, "blocks tile the wave");
   static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8, "row blocks");
@@ -286,12 +318,177 @@ __host__ inline bool buffer_offsets_fit(int bm, int bn, int bk, long long lda, l
   return bk * lda + bm < lim && bn * ldb + bk < lim;
 }
 
+// Rows of C below the last whole tile row, when there are only a few of
+// them: computing them as tiles would run a full tile's K loop for those
+// rows.  Rows [i0, i0 + r) (r at most kStripRows) of a block of columns per
+// workgroup of NT threads.  The NW waves form `cgw` groups of columns (each
+// wave sums SCW columns) and NW/cgw groups along K; the launcher picks cgw
+// so that there are at least as many workgroups as compute units, which
+// spreads the strip's memory traffic evenly (beside tiles, a few heavy strip
+// workgroups would slow the tiles they share a compute unit with).  With
+// several column groups the strip of A passes through LDS in chunks of KC
+// inner indices (staged once per workgroup, the r values of an inner index
+// contiguous, and read by every column group); with one, each lane loads its
+// own values of A directly.  A lane sums its inner indices in order, one fused
+// multiply-add per step and the loads of U steps issued together; the lanes
+// of a wave are then added by a butterfly of exchanges (which leaves the same
+// total in every lane: each addition pairs the same two values on both
+// lanes), and the K groups in order through LDS.  Deterministic.  The row
+// count is a compile-time constant of the loop (one instance per r), so the
+// sums take r x SCW registers.
+constexpr int kStripRows = 8;
+
+// Columns per wave for r rows: as many as keep the r x SCW sums within `acc`
+// elements, at most sc_max.
+__host__ __device__ constexpr int strip_cols(int r, int sc_max, int acc) {
+  return acc / r < 1 ? 1 : (acc / r > sc_max ? sc_max : acc / r);
+}
+
+// Column groups per strip workgroup of nw waves, sc columns each, for n
+// columns on `units` compute units: the most (a power of two dividing nw)
+// that still leaves at least `units` workgroups, else 1.
+__host__ __device__ inline int strip_groups(int n, int sc, int nw, int units) {
+  int g = 1;
+  while (g * 2 <= nw && nw % (g * 2) == 0 && (n + 2 * g * sc - 1) / (2 * g * sc) >= units) g *= 2;
+  return g;
+}
+
+template <typename T, int NT, int SCW, int R, int LDSE>
+__device__ __forceinline__ void strip_rows_r(const GemmArgs<T>& g, int i0, int wg, T* lds) {
+  constexpr int NW = NT / 64;
+  constexpr int PART = NW * R * SCW;             // K-group sums, after the chunk
+  constexpr int KC = (LDSE - PART) / R / 64 * 64;
+  static_assert(KC >= 64, "an A chunk covers a wave's lanes");
+  constexpr int U = (R <= 2 && R * SCW * (int)sizeof(T) <= 32) ? 4 : 2;
+  // wave-uniform (scalar) wave index and group counts, so that the column
+  // addresses below stay in scalar registers and each load takes a 32-bit
+  // lane offset
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int cgw = __builtin_amdgcn_readfirstlane(g.strip_cgw);
+  const int cg = wave % cgw, kg = wave / cgw, kstep = 64 * (NW / cgw);
+  const int j0 = (wg * cgw + cg) * SCW;          // this wave's first column
+  const int nc = g.N - j0 < SCW ? g.N - j0 : SCW;  // its columns inside C (may be <= 0)
+  T* const As = lds;                             // [KC][R]
+  T* const part = lds + KC * R;                  // [NW][R][SCW]
+  T acc[R][SCW];
+#pragma unroll
+  for (int q = 0; q < R; ++q)
+#pragma unroll
+    for (int c = 0; c < SCW; ++c) acc[q][c] = T(0);
+  if (cgw == 1) {
+    // one column group: every inner index is used by one wave only, so each
+    // lane loads its own values of A (the R rows of one inner index are
+    // contiguous: one or two vector loads), with B's, U steps at a time
+    const T* bcol[SCW];
+#pragma unroll
+    for (int c = 0; c < SCW; ++c) bcol[c] = g.B + (size_t)(j0 + (c < nc ? c : 0)) * g.ldb;
+    const T* const arow = g.A + i0;
+#pragma unroll U
+    for (int k = kg * 64 + lane; k < g.K; k += kstep) {
+      T b[SCW];
+#pragma unroll
+      for (int c = 0; c < SCW; ++c) b[c] = c < nc ? bcol[c][k] : T(0);
+      T a[R];
+      __builtin_memcpy(a, arow + (size_t)k * g.lda, sizeof(a));
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int c = 0; c < SCW; ++c) acc[q][c] = __builtin_fma(a[q], b[c], acc[q][c]);
+    }
+  } else {
+  for (int k0 = 0; k0 < g.K; k0 += KC) {
+    const int kc = g.K - k0 < KC ? g.K - k0 : KC;
+    if (k0 > 0) __syncthreads();                 // every wave is done with the last chunk
+    for (int e = t; e < kc * R; e += NT) {
+      const int k = e / R, q = e - k * R;
+      As[e] = g.A[(size_t)(k0 + k) * g.lda + i0 + q];
+    }
+    __syncthreads();
+    if (nc > 0) {
+      const T* bcol[SCW];                        // column c of B at inner index k0
+#pragma unroll
+      for (int c = 0; c < SCW; ++c) bcol[c] = g.B + (size_t)(j0 + (c < nc ? c : 0)) * g.ldb + k0;
+#pragma unroll U
+      for (int k = kg * 64 + lane; k < kc; k += kstep) {
+        T b[SCW];
+#pragma unroll
+        for (int c = 0; c < SCW; ++c) b[c] = c < nc ? bcol[c][k] : T(0);
+        T a[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) a[q] = As[k * R + q];
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+#pragma unroll
+          for (int c = 0; c < SCW; ++c) acc[q][c] = __builtin_fma(a[q], b[c], acc[q][c]);
+      }
+    }
+  }
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q)
+#pragma unroll
+    for (int c = 0; c < SCW; ++c)
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc[q][c] += __shfl_xor(acc[q][c], off, 64);
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+#pragma unroll
+      for (int c = 0; c < SCW; ++c) part[(wave * R + q) * SCW + c] = acc[q][c];
+  }
+  __syncthreads();
+  // thread (cg', q, c) adds the K groups' sums of its column in order
+  const int kgw = NW / cgw;
+  if (t < cgw * R * SCW) {
+    const int g_ = t / (R * SCW), q = (t / SCW) % R, c = t % SCW;
+    const int col = (wg * cgw + g_) * SCW + c;
+    if (col < g.N) {
+      T sum = part[(g_ * R + q) * SCW + c];
+      for (int w = 1; w < kgw; ++w) sum += part[((w * cgw + g_) * R + q) * SCW + c];
+      T* pc = g.C + (size_t)col * g.ldc + (i0 + q);
+      T v = g.alpha * sum;
+      if (g.beta != T(0)) v = __builtin_fma(g.beta, *pc, v);
+      *pc = v;
+    }
+  }
+}
+
+// The strip of r rows for workgroup `wg`, with LDSE elements of LDS at lds.
+template <typename T, int NT, int SCMAX, int ACC, int LDSE>
+__device__ __forceinline__ void strip_rows_wg(const GemmArgs<T>& g, int i0, int r, int wg,
+                                              T* lds) {
+  switch (r) {
+#define PGEMM_STRIP_CASE(RR)                                                        \
+  case RR:                                                                          \
+    strip_rows_r<T, NT, strip_cols(RR, SCMAX, ACC), RR, LDSE>(g, i0, wg, lds);     \
+    break;
+    PGEMM_STRIP_CASE(1)
+    PGEMM_STRIP_CASE(2)
+    PGEMM_STRIP_CASE(3)
+    PGEMM_STRIP_CASE(4)
+    PGEMM_STRIP_CASE(5)
+    PGEMM_STRIP_CASE(6)
+    PGEMM_STRIP_CASE(7)
+    default:
+      strip_rows_r<T, NT, strip_cols(8, SCMAX, ACC), 8, LDSE>(g, i0, wg, lds);
+      break;
+#undef PGEMM_STRIP_CASE
+  }
+}
+
 // ---------------------------------------------------------------- kernel
 // SKP: the stream-K form (a workgroup may run two pieces, and pieces may go
 // to the workspace); without it every workgroup is one whole tile into C.
+// STRIPF: the last g.strip_wgs workgroups of the grid compute the rows below
+// the tiles (strip_rows_wg) instead of a tile.  Being last, they are
+// dispatched as the last round of tiles starts and run beside it on compute
+// units whose LDS has room for a second workgroup, rather than after the
+// whole grid as a kernel of their own would.
 template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS,
-          bool SKP>
-__global__ void __launch_bounds__(WGM * WGN * 64 * KS)
+          bool SKP, bool STRIPF = false>
+__global__ void __launch_bounds__(WGM * WGN * 64 * KS) __attribute__((amdgpu_waves_per_eu(
+    STRIPF ? TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>::LDS_OCC : 1)))
 gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>;
   using T = typename TR::T;
@@ -305,6 +502,15 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   // LDS: the A stages, then the B stages (so that, with a compile-time
   // stage, an access is one per-thread base plus an immediate offset).
   __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+
+  if constexpr (STRIPF) {
+    const int first = g.full_tiles + g.sk_wgs;
+    if ((int)blockIdx.x >= first) {
+      strip_rows_wg<T, NT, Cfg::STRIP_SCMAX, Cfg::STRIP_ACC, Cfg::LDS_ELEMS>(
+          g, g.M, g.strip_rows, (int)blockIdx.x - first, lds);
+      return;
+    }
+  }
 
   // Pieces of work of this workgroup: a tile, a range [kt_begin, kt_end) of
   // its K tiles and a destination (C, or a workspace slot for partial sums).
@@ -446,6 +652,24 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // Lane roles in the matrix instruction.
     const int lrow = lane % MB;   // block row (A) / block column (B) of this lane
     const int kslot = lane / MB;  // which inner-index slot of the instruction
+
+    // Old C of the tile, in the staged epilogue's layout: chunk q = c*NI + i
+    // of this lane is rows rc*V .. rc*V+V-1 of column col of column block c
+    // of the wave tile, with lane + 64*i = col*CPC + rc.  Loaded during the
+    // last K tiles when beta != 0 and the whole tile lies inside C (pf_c),
+    // one chunk per K tile, so that the reads of every tile's C spread over
+    // the end of the K loop instead of all arriving in the epilogue at once.
+    constexpr bool PF_C = Cfg::PF_C && !SKP;
+    constexpr int NPF = PF_C ? Cfg::NPF_C : 1;
+    chunk_t cpf[NPF];
+    const bool pf_c = PF_C && slot < 0 && full_mn && g.beta != T(0);
+    bool pf_done = false;
+    auto load_c_chunk = [&](const int q) __attribute__((always_inline)) {
+      const int c = q / Cfg::EPI_NI, qq = lane + 64 * (q % Cfg::EPI_NI);
+      const int col = qq / Cfg::EPI_CPC, rc = qq % Cfg::EPI_CPC;
+      return load_chunk_full<TR, VEC>(g.C + (size_t)(n0 + wcol + c * MB + col) * g.ldc +
+                                      (m0 + wrow + rc * V));
+    };
 
     // Operands of one group of KG inner indices: CB chunks of B (V inner
     // indices each) and, for each of the V steps, the RB row values of A.
@@ -602,17 +826,23 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       // The steady state is unrolled by S, so that every stage index is a
       // compile-time constant and each LDS access is a per-thread base plus an
       // immediate offset (no address arithmetic per iteration).
-      auto fast_iteration = [&](const int st, const int kt) __attribute__((always_inline)) {
+      // qc: the chunk of old C this iteration loads (-1: none).
+      auto fast_iteration = [&](const int st, const int kt, auto qc) __attribute__((always_inline)) {
+        constexpr int QC = decltype(qc)::value;
         const int st_next = (st + 1 == S) ? 0 : st + 1;
         const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
         read_ops(st, kg0 + KG, ops[1]);
         if constexpr (!RIL) __builtin_amdgcn_sched_barrier(0);
         lstore(st_store);
         gload_full(kt + S);
+        // after the tile's own loads, so that waiting for those (in issue
+        // order) never waits for this one
+        if constexpr (QC >= 0) cpf[QC] = load_c_chunk(QC);
         mma(ops[0]);
         if constexpr (INTERLEAVE) {
           // spread evenly: SP MFMAs before each read, store and load
-          constexpr int NM = (RIL ? N_RD : 0) + N_WR + N_LD;
+          constexpr int N_LDI = N_LD + ((QC >= 0 && MPG >= N_WR + N_LD + 1) ? 1 : 0);
+          constexpr int NM = (RIL ? N_RD : 0) + N_WR + N_LDI;
           constexpr int SP = MPG / NM;
           if constexpr (RIL) {
   #pragma unroll
@@ -627,7 +857,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
           }
   #pragma unroll
-          for (int i = 0; i < N_LD; ++i) {
+          for (int i = 0; i < N_LDI; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
           }
@@ -646,15 +876,35 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         }
         __syncthreads();
       };
+      using NoC = std::integral_constant<int, -1>;
       // st == 0 here (kt == kt_begin), and after every S iterations
       if constexpr (Cfg::UNROLL) {
-        for (; kt + S <= kt_fast_end; kt += S)
+        // With pf_c, the last PF_ITERS whole trips before kt_fast_end (or
+        // later) load the old C, one chunk per iteration.
+        constexpr int PI = Cfg::PF_ITERS;
+        const bool pf_loop = pf_c && kt_fast_end - kt_begin >= PI;
+        const int kt_main_end =
+            pf_loop ? kt_begin + (kt_fast_end - kt_begin - PI) / S * S : kt_fast_end;
+        for (; kt + S <= kt_main_end; kt += S)
           static_for<0, S>([&](auto st_c) {
-            fast_iteration(decltype(st_c)::value, kt + decltype(st_c)::value);
+            fast_iteration(decltype(st_c)::value, kt + decltype(st_c)::value, NoC{});
           });
+        if constexpr (PF_C) {
+          if (pf_loop) {
+            static_for<0, PI / S>([&](auto trip) {
+              static_for<0, S>([&](auto st_c) {
+                constexpr int q = decltype(trip)::value * S + decltype(st_c)::value;
+                fast_iteration(decltype(st_c)::value, kt + decltype(st_c)::value,
+                               std::integral_constant<int, (q < NPF ? q : -1)>{});
+              });
+              kt += S;
+            });
+            pf_done = true;
+          }
+        }
       }
       for (; kt < kt_fast_end; ++kt) {
-        fast_iteration(st, kt);
+        fast_iteration(st, kt, NoC{});
         st = (st + 1 == S) ? 0 : st + 1;
       }
       // Remaining iterations (edge tiles, the K tail, the last S tiles).
@@ -761,7 +1011,16 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
                                             (row_base + rc * V));
         }
       };
-      if (pre_c) load_c_block(0, cpre[0]);
+      if constexpr (PF_C) {
+        // the K loop was too short to load the old C: every chunk now
+        static_assert(NI == Cfg::EPI_NI && NPF == CB * NI, "prefetch layout is the epilogue's");
+        if (pre_c && !pf_done) {
+  #pragma unroll
+          for (int q = 0; q < NPF; ++q) cpf[q] = load_c_chunk(q);
+        }
+      } else {
+        if (pre_c) load_c_block(0, cpre[0]);
+      }
   #pragma unroll
       for (int c = 0; c < CB; ++c) {
   #pragma unroll
@@ -784,16 +1043,21 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the staging is written
         if (pre_c) {
-          if (c + 1 < CB) load_c_block(c + 1, cpre[(c + 1) & 1]);
+          if constexpr (!PF_C) {
+            if (c + 1 < CB) load_c_block(c + 1, cpre[(c + 1) & 1]);
+          }
   #pragma unroll
           for (int i = 0; i < NI; ++i) {
             const int q = lane + 64 * i;
             const int col = q / CPC, rc = q % CPC;
             const chunk_t v =
                 *reinterpret_cast<const chunk_t*>(stg + col * LDW + (rc ^ (col & 7)) * V);
+            chunk_t cold;
+            if constexpr (PF_C) cold = cpf[c * NI + i];
+            else cold = cpre[c & 1][i];
             chunk_t out;
   #pragma unroll
-            for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cpre[c & 1][i][e], alpha * v[e]);
+            for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cold[e], alpha * v[e]);
             store_chunk<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc + (row_base + rc * V),
                                  out);
           }
@@ -1038,76 +1302,25 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs<T> g, int bm, in
   *pc = v;
 }
 
-// Rows of C below the last whole tile row, when there are only a few of
-// them: computing them as tiles would run a full tile's K loop for those
-// rows.  Rows [i0, M) (at most kStripRows), kStripCols consecutive columns
-// per workgroup of kStripThreads threads: thread t sums inner indices t,
-// t + kStripThreads, ... in order (a fused multiply-add per step, the loads
-// of four steps issued together; each value of A, one cache line per inner
-// index, serves all the workgroup's columns), then the partial sums are
-// added by a butterfly of lane exchanges within each wave (which leaves the
-// same total in every lane: each addition pairs the same two values on both
-// lanes) and across the waves in order through LDS.
-constexpr int kStripRows = 8, kStripCols = 8, kStripThreads = 512;
+// The strip of rows below the tile rows as a kernel of its own (for the
+// tile classes whose workgroups leave no room beside them).  g.M is the
+// whole height; rows [i0, g.M) form the strip.
+constexpr int kStripThreads = 512, kStripLdsElems = 8192;
+template <typename T>
+constexpr int strip_kernel_scmax() {
+  return sizeof(T) == 4 ? 8 : 4;
+}
+template <typename T>
+constexpr int strip_kernel_acc() {
+  return sizeof(T) == 4 ? 32 : 16;
+}
 
 template <typename T>
 __global__ void __launch_bounds__(kStripThreads) strip_rows_kernel(GemmArgs<T> g, int i0) {
-  constexpr int NW = kStripThreads / 64;
-  __shared__ T part[NW][kStripRows][kStripCols];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int j0 = blockIdx.x * kStripCols;
-  const int r = g.M - i0;                      // 1 .. kStripRows
-  const int nc = g.N - j0 < kStripCols ? g.N - j0 : kStripCols;
-  T acc[kStripRows][kStripCols];
-#pragma unroll
-  for (int q = 0; q < kStripRows; ++q)
-#pragma unroll
-    for (int c = 0; c < kStripCols; ++c) acc[q][c] = T(0);
-#pragma unroll 4
-  for (int k = t; k < g.K; k += kStripThreads) {
-    T b[kStripCols];
-#pragma unroll
-    for (int c = 0; c < kStripCols; ++c)
-      b[c] = c < nc ? g.B[(size_t)(j0 + c) * g.ldb + k] : T(0);
-    const T* a = g.A + (size_t)k * g.lda + i0;
-#pragma unroll
-    for (int q = 0; q < kStripRows; ++q) {
-      if (q < r) {
-        const T aq = a[q];
-#pragma unroll
-        for (int c = 0; c < kStripCols; ++c) acc[q][c] = __builtin_fma(aq, b[c], acc[q][c]);
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < kStripRows; ++q) {
-    if (q < r) {
-#pragma unroll
-      for (int c = 0; c < kStripCols; ++c) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc[q][c] += __shfl_xor(acc[q][c], off, 64);
-      }
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int q = 0; q < kStripRows; ++q)
-#pragma unroll
-      for (int c = 0; c < kStripCols; ++c) part[wave][q][c] = acc[q][c];
-  }
-  __syncthreads();
-  if (t < kStripRows * kStripCols) {
-    const int q = t / kStripCols, c = t % kStripCols;
-    if (q < r && c < nc) {
-      T sum = part[0][q][c];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) sum += part[w][q][c];
-      T* pc = g.C + (size_t)(j0 + c) * g.ldc + (i0 + q);
-      T v = g.alpha * sum;
-      if (g.beta != T(0)) v = __builtin_fma(g.beta, *pc, v);
-      *pc = v;
-    }
-  }
+  constexpr int LDSE = kStripLdsElems;
+  __shared__ __attribute__((aligned(16))) T lds[LDSE];
+  strip_rows_wg<T, kStripThreads, strip_kernel_scmax<T>(), strip_kernel_acc<T>(), LDSE>(
+      g, i0, g.M - i0, blockIdx.x, lds);
 }
 
 // C <- beta*C on the m x n block (the k == 0 / alpha == 0 path); beta == 0

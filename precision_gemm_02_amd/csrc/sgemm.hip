@@ -8,21 +8,32 @@
 
 namespace pgemm {
 
+// Threads per workgroup and the width limits of a configuration's own strip
+// workgroups (used where it computes strip rows in its grid; see strip_cols).
+#define PGEMM_STRIP_LIMITS(...) \
+  threads_of<__VA_ARGS__>(), strip_scmax_of<__VA_ARGS__>(), strip_acc_of<__VA_ARGS__>()
+
 #define PGEMM_F32(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                        \
-  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, false, \
-   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S>}
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, false, false, \
+   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S>, \
+   PGEMM_STRIP_LIMITS(TraitF32, BM, BN, BK, WM, WN, VEC, S)}
 // The same with the stream-K form compiled in (the tile classes the shape
-// choice uses).
+// choice uses) and with rows below the last whole tile row computed by extra
+// workgroups of the same grid (these classes' LDS leaves room for a second
+// workgroup per compute unit beside a tile).
 #define PGEMM_F32_SK(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                    \
-  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, true, \
-   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 1, true>}
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, true, true, \
+   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 1, true, true>, \
+   PGEMM_STRIP_LIMITS(TraitF32, BM, BN, BK, WM, WN, VEC, S, 1)}
 // _k2: two groups of WM x WN waves split each K tile's inner indices.
 #define PGEMM_F32_K2(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                          \
-  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, false, \
-   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2>}
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, false, false, \
+   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2>, \
+   PGEMM_STRIP_LIMITS(TraitF32, BM, BN, BK, WM, WN, VEC, S, 2)}
 #define PGEMM_F32_K2_SK(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                      \
-  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, true, \
-   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2, true>}
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k2_" #SUFFIX, BM, BN, BK, VEC, true, true, \
+   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2, true, true>, \
+   PGEMM_STRIP_LIMITS(TraitF32, BM, BN, BK, WM, WN, VEC, S, 2)}
 
 // A host function owns the table so that it is never treated as device data.
 const Variant<float>* f32_variants(int* count) {

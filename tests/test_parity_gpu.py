@@ -634,6 +634,114 @@ def test_strip_rows_with_stream_k_random_values(case):
     say("strip+sk random", (m, n, k), "rel %.3g" % rel)
 
 
+# (dtype, m, n, k, workspace?, strip rows, stream-K?): every path of the strip
+# rows, as the library chooses them on 256 compute units -- each tile class
+# under them (the 128 x 128 and 64 x 64 classes compute the strip in extra
+# workgroups of their own grid, the others launch the strip kernel), every
+# row count 1 to 8 that the class reaches, one column group per workgroup
+# (each lane loads its own values of A) and several (the strip of A staged
+# through LDS and shared), and with stream-K of the last round in the same
+# call.
+STRIP_PATH_CASES = [
+    (np.float32, 2433, 3315, 118, False, 1, False),   # f32_128x128x16_w4x2_s4 r=1
+    (np.float32, 385, 8563, 747, False, 1, False),   # f32_128x128x16_w4x2_s4 r=1, 4 column groups
+    (np.float32, 769, 6909, 1324, True, 1, True),   # f32_128x128x16_w4x2_s4 r=1, 2 column groups, stream-K
+    (np.float32, 4994, 1633, 73, False, 2, False),   # f32_128x128x16_w4x2_s4 r=2
+    (np.float32, 1154, 6689, 112, False, 2, False),   # f32_128x128x16_w4x2_s4 r=2, 2 column groups
+    (np.float32, 1794, 5268, 729, True, 2, True),   # f32_128x128x16_w4x2_s4 r=2, 2 column groups, stream-K
+    (np.float32, 2691, 1494, 1820, False, 3, False),   # f32_128x128x16_w4x2_s4 r=3
+    (np.float32, 1539, 5344, 14, False, 3, False),   # f32_128x128x16_w4x2_s4 r=3, 4 column groups
+    (np.float32, 515, 8436, 1390, True, 3, True),   # f32_128x128x16_w4x2_s4 r=3, 4 column groups, stream-K
+    (np.float32, 2436, 1607, 1492, False, 4, False),   # f32_128x128x16_w4x2_s4 r=4
+    (np.float32, 772, 5340, 213, False, 4, False),   # f32_128x128x16_w4x2_s4 r=4, 4 column groups
+    (np.float32, 772, 5511, 936, True, 4, True),   # f32_128x128x16_w4x2_s4 r=4, 4 column groups, stream-K
+    (np.float32, 2693, 1448, 300, False, 5, False),   # f32_128x128x16_w4x2_s4 r=5
+    (np.float32, 1541, 2645, 240, False, 5, False),   # f32_128x128x16_w4x2_s4 r=5, 2 column groups
+    (np.float32, 1285, 3479, 1482, True, 5, True),   # f32_128x128x16_w4x2_s4 r=5, 4 column groups, stream-K
+    (np.float32, 1926, 8657, 12, False, 6, False),   # f32_128x128x16_w4x2_s4 r=6, 8 column groups
+    (np.float32, 1030, 4917, 739, True, 6, True),   # f32_128x128x16_w4x2_s4 r=6, 8 column groups, stream-K
+    (np.float32, 1159, 3273, 476, False, 7, False),   # f32_128x128x16_w4x2_s4 r=7, 4 column groups
+    (np.float32, 903, 4911, 1345, True, 7, True),   # f32_128x128x16_w4x2_s4 r=7, 8 column groups, stream-K
+    (np.float32, 3464, 4721, 74, False, 8, False),   # f32_128x128x16_w4x2_s4 r=8, 8 column groups
+    (np.float32, 1672, 5518, 903, True, 8, True),   # f32_128x128x16_w4x2_s4 r=8, 8 column groups, stream-K
+    (np.float32, 3841, 4242, 10, False, 1, False),   # f32_256x256x16_w2x4_s3 r=1, 2 column groups
+    (np.float32, 3843, 4231, 293, False, 3, False),   # f32_256x256x16_w2x4_s3 r=3, 2 column groups
+    (np.float32, 1796, 8964, 305, False, 4, False),   # f32_256x256x16_w2x4_s3 r=4, 4 column groups
+    (np.float32, 4872, 6431, 44, False, 8, False),   # f32_256x256x16_w2x4_s3 r=8, 4 column groups
+    (np.float32, 577, 1610, 712, False, 1, False),   # f32_64x64x16_w2x2_s4 r=1
+    (np.float32, 129, 8179, 482, False, 1, False),   # f32_64x64x16_w2x2_s4 r=1, 4 column groups
+    (np.float32, 1026, 1021, 932, False, 2, False),   # f32_64x64x16_w2x2_s4 r=2
+    (np.float32, 130, 6879, 399, False, 2, False),   # f32_64x64x16_w2x2_s4 r=2, 4 column groups
+    (np.float32, 4675, 391, 947, False, 3, False),   # f32_64x64x16_w2x2_s4 r=3
+    (np.float32, 195, 4738, 393, False, 3, False),   # f32_64x64x16_w2x2_s4 r=3, 4 column groups
+    (np.float32, 3460, 840, 1464, False, 4, False),   # f32_64x64x16_w2x2_s4 r=4
+    (np.float32, 260, 3942, 176, False, 4, False),   # f32_64x64x16_w2x2_s4 r=4, 4 column groups
+    (np.float32, 453, 4499, 312, False, 5, False),   # f32_64x64x16_w2x2_s4 r=5, 4 column groups
+    (np.float32, 454, 4243, 303, False, 6, False),   # f32_64x64x16_w2x2_s4 r=6, 4 column groups
+    (np.float32, 2055, 508, 366, False, 7, False),   # f32_64x64x16_w2x2_s4 r=7
+    (np.float32, 2183, 2340, 507, False, 7, False),   # f32_64x64x16_w2x2_s4 r=7, 4 column groups
+    (np.float32, 4104, 202, 425, False, 8, False),   # f32_64x64x16_w2x2_s4 r=8
+    (np.float32, 2504, 1608, 555, False, 8, False),   # f32_64x64x16_w2x2_s4 r=8, 4 column groups
+    (np.float32, 1857, 1637, 2293, False, 1, False),   # f32_64x64x32_w2x2_s3_k2 r=1
+    (np.float32, 129, 6010, 1547, False, 1, False),   # f32_64x64x32_w2x2_s3_k2 r=1, 4 column groups
+    (np.float32, 2242, 1855, 1758, False, 2, False),   # f32_64x64x32_w2x2_s3_k2 r=2
+    (np.float32, 258, 3559, 1610, False, 2, False),   # f32_64x64x32_w2x2_s3_k2 r=2, 2 column groups
+    (np.float32, 131, 5765, 539, False, 3, False),   # f32_64x64x32_w2x2_s3_k2 r=3, 8 column groups
+    (np.float32, 1156, 895, 1809, False, 4, False),   # f32_64x64x32_w2x2_s3_k2 r=4
+    (np.float32, 68, 8596, 751, False, 4, False),   # f32_64x64x32_w2x2_s3_k2 r=4, 8 column groups
+    (np.float32, 197, 4236, 369, False, 5, False),   # f32_64x64x32_w2x2_s3_k2 r=5, 8 column groups
+    (np.float32, 134, 6094, 965, False, 6, False),   # f32_64x64x32_w2x2_s3_k2 r=6, 8 column groups
+    (np.float32, 519, 3600, 800, False, 7, False),   # f32_64x64x32_w2x2_s3_k2 r=7, 8 column groups
+    (np.float32, 136, 5714, 271, False, 8, False),   # f32_64x64x32_w2x2_s3_k2 r=8, 8 column groups
+    (np.float64, 2689, 1492, 631, False, 1, False),   # f64_128x128x16_w2x4_s3 r=1
+    (np.float64, 4609, 6241, 34, False, 1, False),   # f64_128x128x16_w2x4_s3 r=1, 4 column groups
+    (np.float64, 2562, 6501, 187, False, 2, False),   # f64_128x128x16_w2x4_s3 r=2, 4 column groups
+    (np.float64, 1667, 7494, 39, False, 3, False),   # f64_128x128x16_w2x4_s3 r=3, 4 column groups
+    (np.float64, 2308, 1747, 2049, False, 4, False),   # f64_128x128x16_w2x4_s3 r=4
+    (np.float64, 4868, 8409, 12, False, 4, False),   # f64_128x128x16_w2x4_s3 r=4, 8 column groups
+    (np.float64, 2949, 1402, 1971, False, 5, False),   # f64_128x128x16_w2x4_s3 r=5
+    (np.float64, 3973, 4211, 132, False, 5, False),   # f64_128x128x16_w2x4_s3 r=5, 4 column groups
+    (np.float64, 4614, 4453, 206, False, 6, False),   # f64_128x128x16_w2x4_s3 r=6, 8 column groups
+    (np.float64, 4871, 5070, 53, False, 7, False),   # f64_128x128x16_w2x4_s3 r=7, 8 column groups
+    (np.float64, 776, 5043, 469, False, 8, False),   # f64_128x128x16_w2x4_s3 r=8, 8 column groups
+    (np.float64, 1217, 805, 1359, False, 1, False),   # f64_64x64x16_w2x4_s4 r=1
+    (np.float64, 385, 2608, 885, False, 1, False),   # f64_64x64x16_w2x4_s4 r=1, 4 column groups
+    (np.float64, 3458, 841, 546, False, 2, False),   # f64_64x64x16_w2x4_s4 r=2
+    (np.float64, 642, 4858, 224, False, 2, False),   # f64_64x64x16_w2x4_s4 r=2, 8 column groups
+    (np.float64, 194, 5684, 848, True, 2, True),   # f64_64x64x16_w2x4_s4 r=2, 8 column groups, stream-K
+    (np.float64, 259, 3400, 120, False, 3, False),   # f64_64x64x16_w2x4_s4 r=3, 8 column groups
+    (np.float64, 707, 3197, 802, True, 3, True),   # f64_64x64x16_w2x4_s4 r=3, 8 column groups, stream-K
+    (np.float64, 132, 5777, 341, False, 4, False),   # f64_64x64x16_w2x4_s4 r=4, 8 column groups
+    (np.float64, 133, 6554, 217, False, 5, False),   # f64_64x64x16_w2x4_s4 r=5, 8 column groups
+    (np.float64, 134, 7771, 134, False, 6, False),   # f64_64x64x16_w2x4_s4 r=6, 8 column groups
+    (np.float64, 390, 2883, 861, True, 6, True),   # f64_64x64x16_w2x4_s4 r=6, 8 column groups, stream-K
+    (np.float64, 2311, 413, 1047, False, 7, False),   # f64_64x64x16_w2x4_s4 r=7
+    (np.float64, 391, 4970, 175, False, 7, False),   # f64_64x64x16_w2x4_s4 r=7, 8 column groups
+    (np.float64, 71, 2852, 1152, True, 7, True),   # f64_64x64x16_w2x4_s4 r=7, 8 column groups, stream-K
+    (np.float64, 392, 2346, 616, False, 8, False),   # f64_64x64x16_w2x4_s4 r=8, 8 column groups
+    (np.float64, 72, 2059, 1649, True, 8, True),   # f64_64x64x16_w2x4_s4 r=8, 8 column groups, stream-K
+]
+
+
+@pytest.mark.parametrize("case", range(len(STRIP_PATH_CASES)))
+def test_strip_paths_exact_integer(case):
+    dtype, m, n, k, use_ws, rows, sk = STRIP_PATH_CASES[case]
+    alpha, beta = ALPHA_BETA[case % len(ALPHA_BETA)]
+    chunk = 4 if dtype == np.float32 else 2
+    lds = leading_dims(m, k, case % 2 == 1, chunk, case)
+    p = exact_problem(dtype, m, n, k, alpha, beta, lds, seed=1300 + case)
+    sel = pg.select_ws_f32 if dtype == np.float32 else pg.select_ws_f64
+    dA, dB, dC = DevMat(p.A), DevMat(p.B), DevMat(p.C)
+    v, sk_wgs, strip = sel(m, n, k, alpha, dA.ptr, p.lda, dB.ptr, p.ldb, beta, dC.ptr, p.ldc,
+                           ws_size(p) if use_ws else 0)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert strip == rows and (sk_wgs > 0) == sk, (strip, sk_wgs)
+    say("strip path", pg.variants()[v], (m, n, k), lds, (alpha, beta), "rows", strip, "sk",
+        sk_wgs)
+    C = run_ws(p) if use_ws else run_colmajor(p)[0]
+    assert_bitwise(C, oracle_full(p))
+
+
 def test_strip_rows_beta_zero_ignores_nan_in_c():
     """beta == 0: the strip rows, like the tiles, never read C."""
     p = exact_problem(np.float32, 4097, 3001, 1023, 1.0, 0.0, (4098, 1024, 4100), seed=970)
