@@ -85,7 +85,7 @@ struct Tables {
   const Variant<float>* f32;
   const Variant<double>* f64;
   int n32, n64;
-  TileClass f32c[5];
+  TileClass f32c[6];
   TileClass f64c[2];
   Tables() {
     f32 = f32_variants(&n32);
@@ -119,6 +119,15 @@ struct Tables {
     // one-group class is up to 12 % faster).
     f32c[4] = {find_variant(f32, n32, "f32_64x64x32_w2x2_s3_k2_vec"),
                find_variant(f32, n32, "f32_64x64x32_w2x2_s3_k2_ua"), 0.96, 1.9e-6};
+    // 32 x 32 tiles in four K groups of one wave (one per SIMD), which hand
+    // their partial sums over through LDS: problems too small to give every
+    // compute unit a 64 x 64 tile.  Fitted to one round of tiles at 128^3,
+    // 256^3 and 512^3 (4.2, 5.1 and 7.1 us against 5.2, 7.1 and 10.7 for
+    // 64 x 64 tiles): ~0.44 of peak in the K loop (one 32 x 32 block per
+    // wave) and ~1 us more per round; from 768^3 on the 64 x 64 classes
+    // are faster (14.5 against 15.2 us).
+    f32c[5] = {find_variant(f32, n32, "f32_32x32x64_w1x1_s3_k4_vec"),
+               find_variant(f32, n32, "f32_32x32x64_w1x1_s3_k4_ua"), 0.44, 1.0e-6};
     // fp64: 128 x 128 tiles for large problems.  Their 64 x 32 wave tiles
     // leave registers for the unrolled steady-state loop, which more than
     // pays for the extra operand traffic of smaller tiles (4096^3: 74.0
@@ -337,7 +346,7 @@ Choice choose(int m, int n, int k, bool sk_ok) {
   if constexpr (sizeof(T) == 4) {
     table = t.f32;
     cls = t.f32c;
-    ncls = 5;
+    ncls = 6;
   } else {
     table = t.f64;
     cls = t.f64c;

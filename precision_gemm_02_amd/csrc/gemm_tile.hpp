@@ -159,8 +159,12 @@ __host__ __device__ inline int swz(int n) {
     return (((n >> 1) ^ (n >> 3)) & 1) | (((n >> 2) & 1) << 1);
   } else if constexpr (KC == 8 && MB == 32) {
     return (n & 7) ^ ((n >> 3) & 1);
+  } else if constexpr (KC == 16 && MB == 32) {
+    // a row is a whole bank line: rows 0-7 with 24-31 and 8-15 with 16-23
+    // (each read cycle's lanes) take 16 distinct chunk positions
+    return n & 15;
   } else {
-    static_assert(KC == 8 && MB == 16, "Bs rows of 4 or 8 chunks; 16 x 16 or 32 x 32 blocks");
+    static_assert(KC == 8 && MB == 16, "Bs rows of 4, 8 or 16 chunks; 16 x 16 or 32 x 32 blocks");
     return n & 7;
   }
 }
@@ -180,7 +184,7 @@ struct TileCfg {
   static constexpr int A_CHUNKS = A_STAGE / V, B_CHUNKS = B_STAGE / V;
   static constexpr int A_LOADS = A_CHUNKS / NT, B_LOADS = B_CHUNKS / NT;
   // Epilogue staging: one region of MB columns x WM rows per wave that
-  // writes C (KS == 2: group 0 only); chunks XOR-swizzled within a column.
+  // writes C (KS > 1: group 0 only); chunks XOR-swizzled within a column.
   static constexpr bool STAGED_EPI = sizeof(T) == 4;   // measured: fp64 gains nothing
   static constexpr int EPI_LDW = WM;
   static_assert(WM / V >= 8, "epilogue swizzle needs 8 chunks per column");
@@ -231,9 +235,11 @@ struct TileCfg {
   static_assert(STAGES >= 2, "at least double buffering");
   static_assert(STAGES == 2 || (BK / KG / KS) % 2 == 0,
                 "ring pipeline alternates two operand sets per wave's share of a tile");
-  static_assert(KS == 1 || (KS == 2 && STAGES > 2), "K split in two, ring pipeline only");
-  // K split: group 1's accumulators pass through LDS to group 0 at the end.
-  static_assert(KS == 1 || (WGM * WGN) * RB * CB * TR::NACC * 64 <= LDS_ELEMS,
+  static_assert(KS == 1 || ((KS == 2 || KS == 4) && STAGES > 2),
+                "K split in two or four, ring pipeline only");
+  // K split: groups 1 .. KS-1 pass their accumulators through LDS to group 0
+  // at the end.
+  static_assert(KS == 1 || (KS - 1) * (WGM * WGN) * RB * CB * TR::NACC * 64 <= LDS_ELEMS,
                 "K-split hand-over fits in LDS");
 };
 
@@ -931,33 +937,39 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       }
     }
 
-    if constexpr (KS == 2) {
-      // Group 1 hands its partial sums to group 0 through LDS (lane-linear,
-      // so each register index is one contiguous 256-byte row per wave); group
-      // 0 adds them in a fixed order and runs the epilogue alone.
+    if constexpr (KS > 1) {
+      // Groups 1 .. KS-1 hand their partial sums to group 0 through LDS
+      // (lane-linear, so each register index is one contiguous 256-byte row
+      // per wave; one region per group); group 0 adds them in group order
+      // and runs the epilogue alone.
       constexpr int NREG = RB * CB * TR::NACC;
       __syncthreads();                       // every wave is done with the ring
-      T* red = lds + wave_in * NREG * 64 + lane;
-      if (kgrp == 1) {
+      T* const red = lds + wave_in * NREG * 64 + lane;
+      constexpr int GSTRIDE = WGM * WGN * NREG * 64;   // elements per group's region
+      if (kgrp > 0) {
+        T* const mine = red + (kgrp - 1) * GSTRIDE;
   #pragma unroll
         for (int b = 0; b < RB; ++b)
   #pragma unroll
           for (int c = 0; c < CB; ++c)
   #pragma unroll
-            for (int e = 0; e < TR::NACC; ++e) red[((b * CB + c) * TR::NACC + e) * 64] = acc[b][c][e];
+            for (int e = 0; e < TR::NACC; ++e) mine[((b * CB + c) * TR::NACC + e) * 64] = acc[b][c][e];
       }
       __syncthreads();
       if (kgrp == 0) {
   #pragma unroll
-        for (int b = 0; b < RB; ++b)
+        for (int j = 0; j < KS - 1; ++j)
   #pragma unroll
-          for (int c = 0; c < CB; ++c)
+          for (int b = 0; b < RB; ++b)
   #pragma unroll
-            for (int e = 0; e < TR::NACC; ++e) acc[b][c][e] += red[((b * CB + c) * TR::NACC + e) * 64];
+            for (int c = 0; c < CB; ++c)
+  #pragma unroll
+              for (int e = 0; e < TR::NACC; ++e)
+                acc[b][c][e] += red[j * GSTRIDE + ((b * CB + c) * TR::NACC + e) * 64];
       }
       // the epilogue's staging reuses this LDS: every read of it is done first
       __syncthreads();
-      if (kgrp == 1) return;
+      if (kgrp != 0) return;
     }
 
     // Destination: C, or for a stream-K piece its raw partial sums (alpha = 1,
@@ -1219,9 +1231,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   if constexpr (!SKP) {
     tile_piece(xcd_remap(blockIdx.x, g.full_tiles), 0, nk_all, -1);
   } else {
-    // With two K groups, group 1 leaves a piece after the hand-over (both
-    // groups have passed the same barriers) while group 0 runs the
-    // epilogue, which has none; both meet again at the barrier below.
+    // With K groups, the groups other than 0 leave a piece after the
+    // hand-over (every group has passed the same barriers) while group 0
+    // runs the epilogue, which has none; all meet again at the barrier below.
     for (int pc = 0; pc < npieces; ++pc) {
       int t_lin, kb = 0, ke = nk_all, slot = -1;
       if (!sk_wg) {

@@ -35,6 +35,12 @@ namespace pgemm {
    &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 2, true, true>, \
    PGEMM_STRIP_LIMITS(TraitF32, BM, BN, BK, WM, WN, VEC, S, 2)}
 
+// _k4: four groups of WM x WN waves split each K tile's inner indices.
+#define PGEMM_F32_K4(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                          \
+  {"f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_k4_" #SUFFIX, BM, BN, BK, VEC, false, false, \
+   &launch_tile<TraitF32, BM, BN, BK, WM, WN, VEC, S, 4>, \
+   PGEMM_STRIP_LIMITS(TraitF32, BM, BN, BK, WM, WN, VEC, S, 4)}
+
 // A host function owns the table so that it is never treated as device data.
 const Variant<float>* f32_variants(int* count) {
   static const Variant<float> table[] = {
@@ -73,6 +79,13 @@ const Variant<float>* f32_variants(int* count) {
       // compute unit, where one wave per SIMD cannot hide the memory latency
       PGEMM_F32_K2_SK(64, 64, 32, 2, 2, 3, true, vec),
       PGEMM_F32_K2_SK(64, 64, 32, 2, 2, 3, false, ua),
+      // 32 x 32 tiles, four K groups of one wave (one per SIMD); and 64 x 64
+      // tiles, four K groups of 4 waves (16 waves, four per SIMD): small
+      // problems, where tiles per compute unit, not operand traffic, decide
+      PGEMM_F32_K4(32, 32, 64, 1, 1, 3, true, vec),
+      PGEMM_F32_K4(32, 32, 64, 1, 1, 3, false, ua),
+      PGEMM_F32_K4(64, 64, 64, 2, 2, 3, true, vec),
+      PGEMM_F32_K4(64, 64, 64, 2, 2, 3, false, ua),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -459,7 +459,7 @@ def run_ws(p, ws_bytes=None):
 # Together they cover every tile class with a stream-K form in both
 # precisions, last rounds below and above half full and no full round at
 # all, aligned and crossing plans, fewer workgroups than compute units,
-# ragged M/N edges and K tails inside the shared tiles, and up to 25 pieces
+# ragged M/N edges and K tails inside the shared tiles, and up to 50 pieces
 # summed per tile.
 SK_SHAPES = [
     (np.float32, 2150, 2030, 1000),    # 128^2: 256 + 16, S 240 aligned, K tail 8
@@ -474,7 +474,7 @@ SK_SHAPES = [
     (np.float64, 9224, 73, 539),       # fp64 64^2: 256 + 34, S 238 aligned, K tail 11
     # no full round: every tile shared (at least 2 K tiles per workgroup)
     (np.float32, 67, 4253, 2126),      # 134 edge tiles of 64^2, crossing, K tail 14
-    (np.float32, 66, 93, 794),         # 4 edge tiles, S 100, 25 pieces each, K tail 10
+    (np.float32, 66, 93, 1610),        # 4 edge tiles, S 200, 50 pieces each, K tail 10
     (np.float32, 2885, 68, 1923),      # 92 edge tiles, crossing, K tail 3
     (np.float64, 65, 2145, 1849),      # 68 fp64 edge tiles, crossing, K tail 9
     (np.float64, 136, 83, 606),        # 6 fp64 edge tiles, S 114, 19 pieces each
@@ -556,6 +556,8 @@ CLASS_CASES = [
     (np.float32, 1000, 700, 900, (1001, 901, 1003), "f32_64x64x16_w2x2_s4_ua"),
     (np.float32, 1000, 1000, 3000, (1000, 3000, 1000), "f32_64x64x32_w2x2_s3_k2_vec"),
     (np.float32, 1001, 999, 2500, (1002, 2501, 1004), "f32_64x64x32_w2x2_s3_k2_ua"),
+    (np.float32, 512, 512, 512, (512, 512, 512), "f32_32x32x64_w1x1_s3_k4_vec"),
+    (np.float32, 257, 301, 199, (258, 200, 259), "f32_32x32x64_w1x1_s3_k4_ua"),
     (np.float64, 2048, 2048, 512, (2050, 514, 2048), "f64_128x128x16_w2x4_s3_vec"),
     (np.float64, 2048, 2047, 511, (2049, 512, 2051), "f64_128x128x16_w2x4_s3_ua"),
     (np.float64, 700, 900, 500, (700, 500, 702), "f64_64x64x16_w2x4_s4_vec"),
