@@ -288,7 +288,7 @@ def recorded_counters(variant: str, workload: str):
         return None
     return {"mfma_util": float(kv["mfma_util"]),
             "lds_bank_conflict_cycles": float(kv["lds_bank_conflict_cycles"]),
-            "source": "rocprofv3 --pmc, profiles/ (same built library)"}
+            "source": "rocprofv3 --pmc, profiles/ (same kernel sources and build flags)"}
 
 
 def device_peak(dt: str):
