@@ -361,7 +361,8 @@ def cpu_baseline(p, first_out: np.ndarray, seconds: float):
 
 
 def sweep(args):
-    """Every workload: GPU kernel time (median of event-timed launches), the
+    """Every workload: GPU time per call (two HIP events on the launch stream
+    around a run of back-to-back launches, about 50 ms of GPU time), the
     parity figures against the oracle (full result up to 4096^3, the first
     columns at 8192^3) and the oracle's time on the same columns."""
     import torch
@@ -387,7 +388,7 @@ def sweep(args):
             got = gi.logical_colmajor(out, p.m, p.n, p.ldc).astype(np.float64)
         r.reset_c()
         _, per = warm_up(r, args.warmup, args.min_warmup_seconds)
-        _, kern_med = timed_steps(r, auto_steps(r, max(args.steps, 10), per))
+        _, kern_ms = timed_steps(r, auto_steps(r, max(args.steps, 10), per))
         cold_ms = cold_kernel_ms(r, flush, 5)
         cols = p.n if p.m * p.n * p.k <= 4096 ** 3 else 512
         t0 = time.perf_counter()
@@ -412,8 +413,8 @@ def sweep(args):
         else:
             ok = rel <= 1e-12
         cnt = recorded_counters(r.variant, r.name)
-        tflops = r.flops / (kern_med * 1e-3) / 1e12
-        rows.append((name, "%dx%dx%d" % (p.m, p.n, p.k), r.entry, r.variant, kern_med, tflops,
+        tflops = r.flops / (kern_ms * 1e-3) / 1e12
+        rows.append((name, "%dx%dx%d" % (p.m, p.n, p.k), r.entry, r.variant, kern_ms, tflops,
                      100 * tflops / PEAK_TFLOPS[r.dt], cnt, maxabs, rel, ok, t_or, cols, p.n,
                      2.0 * p.m * cols * p.k / t_or / 1e9, cold_ms,
                      100 * tflops / device_peak(r.dt)[0]))
