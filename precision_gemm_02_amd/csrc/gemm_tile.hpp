@@ -253,6 +253,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Fused multiply-add in the element type: a*b + c rounded once to T.  (The
+// generic __builtin_fma takes doubles: with float operands it would compute
+// in double and round twice.)
+__device__ __forceinline__ float fma_t(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_t(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
 // ---------------------------------------------------------------- loads
 // 16 bytes at p.  VEC: p is 16-byte aligned.  Otherwise p is only element
 // aligned; multi-dword global accesses on gfx950 need dword alignment only,
@@ -382,25 +388,35 @@ __device__ __forceinline__ void strip_rows_r(const GemmArgs<T>& g, int i0, int w
   for (int q = 0; q < R; ++q)
 #pragma unroll
     for (int c = 0; c < SCW; ++c) acc[q][c] = T(0);
+  // Column c of this wave's B columns, clamped into C (N >= 1 here): every
+  // load below is unconditional, so a step's loads issue together and one
+  // wait covers them; the values of columns at or past N are then replaced
+  // by zero (their sums are never stored).
+  const T* bcol[SCW];
+#pragma unroll
+  for (int c = 0; c < SCW; ++c) {
+    const int col = j0 + c < g.N ? j0 + c : g.N - 1;
+    bcol[c] = g.B + (size_t)col * g.ldb;
+  }
   if (cgw == 1) {
     // one column group: every inner index is used by one wave only, so each
     // lane loads its own values of A (the R rows of one inner index are
     // contiguous: one or two vector loads), with B's, U steps at a time
-    const T* bcol[SCW];
-#pragma unroll
-    for (int c = 0; c < SCW; ++c) bcol[c] = g.B + (size_t)(j0 + (c < nc ? c : 0)) * g.ldb;
     const T* const arow = g.A + i0;
 #pragma unroll U
     for (int k = kg * 64 + lane; k < g.K; k += kstep) {
       T b[SCW];
 #pragma unroll
-      for (int c = 0; c < SCW; ++c) b[c] = c < nc ? bcol[c][k] : T(0);
+      for (int c = 0; c < SCW; ++c) {
+        const T v = bcol[c][k];
+        b[c] = c < nc ? v : T(0);
+      }
       T a[R];
       __builtin_memcpy(a, arow + (size_t)k * g.lda, sizeof(a));
 #pragma unroll
       for (int q = 0; q < R; ++q)
 #pragma unroll
-        for (int c = 0; c < SCW; ++c) acc[q][c] = __builtin_fma(a[q], b[c], acc[q][c]);
+        for (int c = 0; c < SCW; ++c) acc[q][c] = fma_t(a[q], b[c], acc[q][c]);
     }
   } else {
   for (int k0 = 0; k0 < g.K; k0 += KC) {
@@ -412,21 +428,21 @@ __device__ __forceinline__ void strip_rows_r(const GemmArgs<T>& g, int i0, int w
     }
     __syncthreads();
     if (nc > 0) {
-      const T* bcol[SCW];                        // column c of B at inner index k0
-#pragma unroll
-      for (int c = 0; c < SCW; ++c) bcol[c] = g.B + (size_t)(j0 + (c < nc ? c : 0)) * g.ldb + k0;
 #pragma unroll U
       for (int k = kg * 64 + lane; k < kc; k += kstep) {
         T b[SCW];
 #pragma unroll
-        for (int c = 0; c < SCW; ++c) b[c] = c < nc ? bcol[c][k] : T(0);
+        for (int c = 0; c < SCW; ++c) {
+          const T v = bcol[c][k0 + k];
+          b[c] = c < nc ? v : T(0);
+        }
         T a[R];
 #pragma unroll
         for (int q = 0; q < R; ++q) a[q] = As[k * R + q];
 #pragma unroll
         for (int q = 0; q < R; ++q)
 #pragma unroll
-          for (int c = 0; c < SCW; ++c) acc[q][c] = __builtin_fma(a[q], b[c], acc[q][c]);
+          for (int c = 0; c < SCW; ++c) acc[q][c] = fma_t(a[q], b[c], acc[q][c]);
       }
     }
   }
@@ -454,7 +470,7 @@ __device__ __forceinline__ void strip_rows_r(const GemmArgs<T>& g, int i0, int w
       for (int w = 1; w < kgw; ++w) sum += part[((w * cgw + g_) * R + q) * SCW + c];
       T* pc = g.C + (size_t)col * g.ldc + (i0 + q);
       T v = g.alpha * sum;
-      if (g.beta != T(0)) v = __builtin_fma(g.beta, *pc, v);
+      if (g.beta != T(0)) v = fma_t(g.beta, *pc, v);
       *pc = v;
     }
   }
@@ -1069,7 +1085,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
             else cold = cpre[c & 1][i];
             chunk_t out;
   #pragma unroll
-            for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cold[e], alpha * v[e]);
+            for (int e = 0; e < V; ++e) out[e] = fma_t(beta, cold[e], alpha * v[e]);
             store_chunk<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc + (row_base + rc * V),
                                  out);
           }
@@ -1089,7 +1105,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
               if (read_c) {
                 const chunk_t cv = load_chunk_full<TR, VEC>(pc);
   #pragma unroll
-                for (int e = 0; e < V; ++e) out[e] = __builtin_fma(beta, cv[e], alpha * v[e]);
+                for (int e = 0; e < V; ++e) out[e] = fma_t(beta, cv[e], alpha * v[e]);
               } else {
   #pragma unroll
                 for (int e = 0; e < V; ++e) out[e] = alpha * v[e];
@@ -1100,7 +1116,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
               for (int e = 0; e < V; ++e) {
                 if (grow + e < m_end) {
                   T o = alpha * v[e];
-                  if (read_c) o = __builtin_fma(beta, pc[e], o);
+                  if (read_c) o = fma_t(beta, pc[e], o);
                   pc[e] = o;
                 }
               }
@@ -1154,7 +1170,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
             T out[RUN];
   #pragma unroll
             for (int o = 0; o < RUN; ++o)
-              out[o] = __builtin_fma(beta, cvb[gq & 1][run][o],
+              out[o] = fma_t(beta, cvb[gq & 1][run][o],
                                      alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W]);
             if constexpr (VEC_C) {
   #pragma unroll
@@ -1192,7 +1208,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   #pragma unroll
               for (int o = 0; o < RUN; ++o) {
                 out[o] = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
-                if (read_c) out[o] = __builtin_fma(beta, cv[run][o], out[o]);
+                if (read_c) out[o] = fma_t(beta, cv[run][o], out[o]);
               }
               if constexpr (VEC_C) {
   #pragma unroll
@@ -1217,7 +1233,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
               for (int o = 0; o < RUN; ++o) {
                 if (row + o < M) {
                   T v = alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W];
-                  if (read_c) v = __builtin_fma(beta, pc[o], v);
+                  if (read_c) v = fma_t(beta, pc[o], v);
                   pc[o] = v;
                 }
               }
@@ -1310,7 +1326,7 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs<T> g, int bm, in
   }
   T* pc = g.C + (size_t)j * g.ldc + i;
   T v = g.alpha * sum;
-  if (g.beta != T(0)) v = __builtin_fma(g.beta, *pc, v);
+  if (g.beta != T(0)) v = fma_t(g.beta, *pc, v);
   *pc = v;
 }
 
