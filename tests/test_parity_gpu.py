@@ -260,6 +260,55 @@ def test_beta_zero_ignores_nan_c(dtype):
         assert_f64_parity(C, R)
 
 
+# fp32: C = alpha*acc + beta*C is one fused multiply-add rounded once in fp32.
+# With acc = 1 + 2^-23 (exact: only k = 0 contributes), alpha = 1,
+# beta = 2^-24 (1 + 2^-23) and C = 1 - 2^-23, the exact result is
+# 1 + 2^-23 + 2^-24 - 2^-70, just below the midpoint of 1 + 2^-23 and
+# 1 + 2^-22: rounded once it is 1 + 2^-23; computed in double and rounded
+# again it lands on the midpoint and ties to 1 + 2^-22.  One shape per path
+# that computes the sum: small tiles, the 128 x 128 staged epilogue with the
+# old C read during the last K tiles, strip rows in the grid's own
+# workgroups, the strip kernel, and the stream-K fix-up.
+ROUNDING_CASES = [
+    ("small tiles", 64, 64, 16, (64, 16, 64), False, None),
+    ("staged epilogue", 2048, 2048, 512, (2048, 512, 2048), False, "f32_128x128x16_w4x2_s4_vec"),
+    ("strip in the grid", 4097, 3001, 1023, (4098, 1024, 4100), False, "strip"),
+    ("strip kernel", 4357, 3791, 16, (4360, 16, 4360), False, "strip"),
+    ("stream-K fix-up", 2150, 2030, 1000, (2150, 1000, 2150), True, "sk"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ROUNDING_CASES)), ids=lambda c: ROUNDING_CASES[c][0])
+def test_fp32_epilogue_rounds_once(case):
+    name, m, n, k, (lda, ldb, ldc), use_ws, path = ROUNDING_CASES[case]
+    one_ulp = np.float32(1 + 2.0 ** -23)
+    av = np.zeros((k, m), np.float32)
+    av[0, :] = one_ulp                       # column 0 of A, column-major values
+    bv = np.zeros((n, k), np.float32)
+    bv[:, 0] = 1                             # row 0 of B
+    cv = np.full(m * n, np.float32(1 - 2.0 ** -23))
+    beta = float(np.float32(2.0 ** -24 * (1 + 2.0 ** -23)))
+    p = gi.Problem("rounding", np.float32, m, n, k, lda, ldb, ldc, 1.0, beta,
+                   gi.colmajor(av.reshape(-1), m, k, lda, np.float32(np.nan)),
+                   gi.colmajor(bv.reshape(-1), k, n, ldb, np.float32(np.nan)),
+                   gi.colmajor(cv, m, n, ldc, gi.C_SENTINEL_F32))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256 and path is not None:
+        dA, dB, dC = DevMat(p.A), DevMat(p.B), DevMat(p.C)
+        v, sk, strip = pg.select_ws_f32(m, n, k, 1.0, dA.ptr, lda, dB.ptr, ldb, beta, dC.ptr,
+                                        ldc, ws_size(p) if use_ws else 0)
+        if path == "strip":
+            assert strip > 0, (name, strip)
+        elif path == "sk":
+            assert sk > 0, (name, sk)
+        else:
+            assert pg.variants()[v] == path, pg.variants()[v]
+    C = run_ws(p) if use_ws else run_colmajor(p)[0]
+    want = np.float32(1 + 2.0 ** -23)
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, (name, len(bad), bad[:4], C[tuple(bad[0])] if len(bad) else None)
+    say("rounding", name, (m, n, k), "all", m * n, "elements", want)
+
+
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_alpha_zero_and_k_zero_scale_c(dtype):
     m, n, ldc = 300, 70, 303
