@@ -898,6 +898,51 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         }
         __syncthreads();
       };
+      // The last S tiles when they are whole and the steady state ends at
+      // stage 0 (K a multiple of S*BK on the fast path): the same iteration
+      // without global loads, the first storing the last tile fetched, and
+      // with compile-time stages like the steady state's (the general loop
+      // below computes LDS addresses and branches at run time, ~15 % slower
+      // per tile).
+      auto drain_iteration = [&](auto st_c) __attribute__((always_inline)) {
+        constexpr int st = decltype(st_c)::value;
+        constexpr bool first = st == 0, last = st == S - 1;
+        // the last tile's prefetch re-reads its own stage (in bounds, unused)
+        constexpr int st_next = last ? st : st + 1;
+        read_ops(st, kg0 + KG, ops[1]);
+        if constexpr (!RIL) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (first) lstore(S - 1);
+        mma(ops[0]);
+        constexpr int N_WRD = first ? N_WR : 0;
+        constexpr int NM = (RIL ? N_RD : 0) + N_WRD;
+        if constexpr (INTERLEAVE && NM > 0) {
+          constexpr int SP = MPG / NM;
+          if constexpr (RIL) {
+  #pragma unroll
+            for (int i = 0; i < N_RD; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            }
+          }
+  #pragma unroll
+          for (int i = 0; i < N_WRD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, MPG - SP * NM, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int gi = 1; gi < NGL; ++gi) {
+          if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
+          else read_ops(st_next, kg0, ops[(gi + 1) & 1]);
+          if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
+          mma(ops[gi & 1]);
+          spread_reads();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+      };
       using NoC = std::integral_constant<int, -1>;
       // st == 0 here (kt == kt_begin), and after every S iterations
       if constexpr (Cfg::UNROLL) {
@@ -928,6 +973,14 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       for (; kt < kt_fast_end; ++kt) {
         fast_iteration(st, kt, NoC{});
         st = (st + 1 == S) ? 0 : st + 1;
+      }
+      // (Not in the kernels with strip workgroups: its registers would cost
+      // their tiles more spills than the drain saves.)
+      if constexpr (Cfg::UNROLL && !STRIPF) {
+        if (st == 0 && kt == kt_fast_end && kt + S == kt_end && kt > kt_begin) {
+          static_for<0, S>([&](auto st_c) { drain_iteration(st_c); });
+          kt = kt_end;
+        }
       }
       // Remaining iterations (edge tiles, the K tail, the last S tiles).
       for (; kt < kt_end; ++kt) {
