@@ -201,8 +201,9 @@ struct TileCfg {
   // live; larger tiles would spill.
   static constexpr bool UNROLL = ACC_REGS + 2 * OPS_REGS + STAGE_REGS <= 192;
   // With beta != 0, the old C of a whole tile can be loaded into registers
-  // during the last K tiles (one 16-byte chunk per lane and K tile) instead
-  // of in the epilogue, when that costs at most 32 registers: the staged
+  // during the last K tiles (one 16-byte chunk per lane and K tile, all but
+  // the last) instead of in the epilogue, when that costs at most 32
+  // registers: the staged
   // epilogue's chunks (MB columns x WM rows per column block, WM/V chunks
   // per column) of the CB column blocks, NPF_C chunks per lane.
   static constexpr int EPI_CPC = WM / V;
@@ -681,6 +682,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // last K tiles when beta != 0 and the whole tile lies inside C (pf_c),
     // one chunk per K tile, so that the reads of every tile's C spread over
     // the end of the K loop instead of all arriving in the epilogue at once.
+    // The last chunk waits for the epilogue: one chunk fewer held through the
+    // K loop keeps the 128 x 128 kernel within the 128 registers that leave
+    // room for a second workgroup per compute unit.
     constexpr bool PF_C = Cfg::PF_C && !SKP;
     constexpr int NPF = PF_C ? Cfg::NPF_C : 1;
     chunk_t cpf[NPF];
@@ -962,7 +966,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
               static_for<0, S>([&](auto st_c) {
                 constexpr int q = decltype(trip)::value * S + decltype(st_c)::value;
                 fast_iteration(decltype(st_c)::value, kt + decltype(st_c)::value,
-                               std::integral_constant<int, (q < NPF ? q : -1)>{});
+                               std::integral_constant<int, (q < NPF - 1 ? q : -1)>{});
               });
               kt += S;
             });
@@ -1099,6 +1103,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   #pragma unroll
           for (int q = 0; q < NPF; ++q) cpf[q] = load_c_chunk(q);
         }
+        if (pre_c && pf_done) cpf[NPF - 1] = load_c_chunk(NPF - 1);   // not prefetched
       } else {
         if (pre_c) load_c_block(0, cpre[0]);
       }
