@@ -202,10 +202,13 @@ def test_ring_pipeline_boundaries(variant):
     dtype = np.float32 if prec == "32" else np.float64
     chunk = 4 if dtype == np.float32 else 2
     # whole K tiles nk: the steady-state loop runs nk - S iterations, first in
-    # trips of S (compile-time stages), then 0..S-1 more with a runtime stage
+    # trips of S (compile-time stages), then 0..S-1 more with a runtime stage;
+    # nk a multiple of S (2S, 3S) ends it at stage 0, where the last S tiles
+    # take the compile-time drain
     Ks = sorted({1, BK - 1, BK * (S - 1), BK * S, BK * S + 1, BK * (S + 1) - 1,
-                 BK * (S + 1), BK * (S + 1) + 1, BK * (S + 2) + 3, BK * (2 * S + 1),
-                 BK * (2 * S + 2), BK * (2 * S + 3), BK * (3 * S + 2) + 5})
+                 BK * (S + 1), BK * (S + 1) + 1, BK * (S + 2) + 3, BK * 2 * S,
+                 BK * (2 * S + 1), BK * (2 * S + 2), BK * (2 * S + 3), BK * 3 * S,
+                 BK * (3 * S + 2) + 5})
     shapes = [(2 * BM, 2 * BN), (2 * BM + 5, BN + 3)]
     t = 0
     for (mm, nn) in shapes:
