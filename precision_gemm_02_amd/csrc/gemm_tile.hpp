@@ -221,7 +221,8 @@ struct TileCfg {
   // share a compute unit.
   // Waves per SIMD that the LDS allows (160 KiB per compute unit, NT/256
   // waves per SIMD per workgroup): the kernels with a strip role ask the
-  // compiler to keep that occupancy.
+  // compiler to keep that occupancy (not their stream-K forms, whose own
+  // piece loop already takes more registers than that occupancy leaves).
   static constexpr int LDS_OCC = (160 * 1024 / LDS_BYTES) * (NT / 256) > 8
                                      ? 8
                                      : (160 * 1024 / LDS_BYTES) * (NT / 256);
@@ -511,7 +512,7 @@ __device__ __forceinline__ void strip_rows_wg(const GemmArgs<T>& g, int i0, int 
 template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS,
           bool SKP, bool STRIPF = false>
 __global__ void __launch_bounds__(WGM * WGN * 64 * KS) __attribute__((amdgpu_waves_per_eu(
-    STRIPF ? TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>::LDS_OCC : 1)))
+    (STRIPF && !SKP) ? TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>::LDS_OCC : 1)))
 gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>;
   using T = typename TR::T;
