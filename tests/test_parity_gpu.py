@@ -263,6 +263,63 @@ def test_beta_zero_ignores_nan_c(dtype):
         assert_f64_parity(C, R)
 
 
+# Inf and NaN in A and B propagate as in IEEE arithmetic: with inputs from
+# U[-1, 1) (no exact zeros, no overflow) every output is finite, +Inf, -Inf or
+# NaN according to which non-finite values meet in its sum, whatever the
+# summation order, so the kernels' classification must equal the oracle's
+# element for element.  Shapes: 32 x 32 tiles in four K groups, 64 x 64 and
+# 128 x 128 tiles with strip rows in the grid, 64 x 64 in two K groups with
+# strip rows, 256 x 128 tiles, the stream-K path, fp64.
+SPECIAL_CASES = [
+    (np.float32, 200, 150, 77, False),
+    (np.float32, 2051, 1000, 300, False),
+    (np.float32, 4097, 3001, 1023, False),
+    (np.float32, 391, 2418, 1564, False),
+    (np.float32, 4097, 1500, 300, False),
+    (np.float32, 2150, 2030, 1000, True),
+    (np.float64, 700, 500, 99, False),
+]
+
+
+def _classify(C):
+    out = np.zeros(C.shape, np.int8)
+    out[np.isposinf(C)] = 1
+    out[np.isneginf(C)] = 2
+    out[np.isnan(C)] = 3
+    return out
+
+
+@pytest.mark.parametrize("case", range(len(SPECIAL_CASES)))
+def test_inf_and_nan_propagate_like_the_oracle(case):
+    dtype, m, n, k, use_ws = SPECIAL_CASES[case]
+    p = gi.make_colmajor_problem("special", dtype, m, n, k, m + 1, k + 2, m + 3, 0.75, -1.25,
+                                 seed=1500 + case, dist="u", c_dist="u")
+    rng = np.random.default_rng(1600 + case)
+    A = gi.logical_colmajor(p.A, m, k, p.lda).copy()
+    B = gi.logical_colmajor(p.B, k, n, p.ldb).copy()
+    for arr, count in ((A, 6), (B, 6)):
+        for t in range(count):
+            i, j = rng.integers(0, arr.shape[0]), rng.integers(0, arr.shape[1])
+            arr[i, j] = (np.inf, -np.inf, np.nan)[t % 3]
+    # the last row and column of A and B too (edge tiles, the K tail)
+    A[m - 1, k - 1] = np.inf
+    B[k - 1, n - 1] = -np.inf
+    p.A = gi.colmajor(A.T.reshape(-1), m, k, p.lda, dtype(np.nan))
+    p.B = gi.colmajor(B.T.reshape(-1), k, n, p.ldb, dtype(np.nan))
+    R = oracle_full(p)
+    C = run_ws(p) if use_ws else run_colmajor(p)[0]
+    got, want = _classify(C), _classify(R)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (len(bad), bad[:4])
+    fin = want == 0
+    assert fin.sum() > m * n // 2          # most outputs stay finite
+    if dtype == np.float32:
+        assert_f32_parity(np.where(fin, C, 0), np.where(fin, R, 0), p.k)
+    else:
+        assert_f64_parity(np.where(fin, C, 0), np.where(fin, R, 0))
+    say("special values", (m, n, k), "non-finite", int((~fin).sum()), "of", m * n)
+
+
 # fp32: C = alpha*acc + beta*C is one fused multiply-add rounded once in fp32.
 # With acc = 1 + 2^-23 (exact: only k = 0 contributes), alpha = 1,
 # beta = 2^-24 (1 + 2^-23) and C = 1 - 2^-23, the exact result is
