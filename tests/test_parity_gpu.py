@@ -263,6 +263,30 @@ def test_beta_zero_ignores_nan_c(dtype):
         assert_f64_parity(C, R)
 
 
+# Very long K loops on tiny outputs (thousands of K tiles, the K tail): the
+# plain entry takes 32 x 32 tiles in four K groups, the workspace entry
+# shares the K tiles by stream-K; integers in {-2..2} keep every partial sum
+# exact (|sum| <= 4K < 2^24), so both must equal the oracle bitwise.
+LONG_K_CASES = [
+    (np.float32, 64, 64, 65537),
+    (np.float32, 33, 7, 100003),
+    (np.float32, 300, 200, 70001),
+    (np.float64, 40, 50, 70001),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LONG_K_CASES)))
+def test_very_long_k_exact_integer(case):
+    dtype, m, n, k = LONG_K_CASES[case]
+    alpha, beta = ALPHA_BETA[case % len(ALPHA_BETA)]
+    p = exact_problem(dtype, m, n, k, alpha, beta, (m + 1, k + 1, m + 2), seed=1700 + case)
+    R = oracle_full(p)
+    assert_bitwise(run_colmajor(p)[0], R)
+    assert ws_size(p) > 0                  # stream-K: the K tiles are shared
+    assert_bitwise(run_ws(p), R)
+    say("long K", (m, n, k), (alpha, beta))
+
+
 # Inf and NaN in A and B propagate as in IEEE arithmetic: with inputs from
 # U[-1, 1) (no exact zeros, no overflow) every output is finite, +Inf, -Inf or
 # NaN according to which non-finite values meet in its sum, whatever the
