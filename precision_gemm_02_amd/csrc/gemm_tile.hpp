@@ -319,6 +319,14 @@ __device__ __forceinline__ typename TR::chunk_t load_chunk_buf(__amdgpu_buffer_r
                             __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// The same 16 bytes written straight to LDS: every lane of the wave writes
+// at lds_wave (the same for all its lanes) + 16 * lane.
+__device__ __forceinline__ void load_chunk_buf_lds(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                                   void* lds_wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_wave, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, kBufferWord3);
 }
@@ -799,13 +807,47 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       // was written S-2 >= 1 barriers earlier, so the MFMAs of the next tile
       // start right after the barrier without waiting for LDS.
       constexpr int S = STAGES;
-      for (int t = 0; t < S - 1; ++t)
-        if (kt_begin + t < kt_end) {
-          gload(kt_begin + t);
-          lstore(t);
+      constexpr int N_LD = A_LOADS + B_LOADS;                        // global loads
+      // Tile kt's chunks straight from memory into LDS stage `stage` (buffer
+      // loads to LDS: lane l of a wave writes 16 bytes at the wave's base +
+      // 16*l, which is the stage layout of chunk q = tid + i*NT; for B the
+      // lane loads the chunk that the swizzle puts at its place).  Whole K
+      // tiles, with the redirected loads of gload_full on the M and N edges.
+      auto dma_tile = [&](const int kt, const int stage) __attribute__((always_inline)) {
+        const int wave_base = (tid & ~63) * V;   // elements
+        T* As = lds + stage * Cfg::A_STAGE + wave_base;
+        T* Bs = lds + STAGES * Cfg::A_STAGE + stage * Cfg::B_STAGE + wave_base;
+        const __amdgpu_buffer_rsrc_t ar = tile_rsrc(a_tile + (size_t)kt * BK * (size_t)lda);
+  #pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) load_chunk_buf_lds(ar, a_off, i * a_step, As + i * NT * V);
+        const __amdgpu_buffer_rsrc_t br = tile_rsrc(b_tile + (size_t)kt * BK);
+  #pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) {
+          const int q = tid + i * NT, nn = q / KC;
+          const int off = (int)(((long long)(n0 + nn < N ? nn : 0) * ldb +
+                                 ((q % KC) ^ swz<KC, TR::MB>(nn)) * V) * TS);
+          load_chunk_buf_lds(br, off, 0, Bs + i * NT * V);
         }
-      if (kt_begin + S - 1 < kt_end) gload(kt_begin + S - 1);
-      __syncthreads();
+      };
+      // The first S-1 tiles whole: all of them in flight at once with tile
+      // S-1's register loads (one memory round trip before the first barrier
+      // instead of one per stage).  Not in the kernels with stream-K pieces or
+      // strip workgroups, whose registers it would raise past their
+      // occupancy (or into spills).
+      if (!SKP && !STRIPF && g.buf32 && edge_fast && kt_begin + S - 1 <= min(kt_end, k_whole)) {
+        for (int t = 0; t < S - 1; ++t) dma_tile(kt_begin + t, t);
+        if (kt_begin + S - 1 < kt_end) gload(kt_begin + S - 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every stage has landed
+        __syncthreads();
+      } else {
+        for (int t = 0; t < S - 1; ++t)
+          if (kt_begin + t < kt_end) {
+            gload(kt_begin + t);
+            lstore(t);
+          }
+        if (kt_begin + S - 1 < kt_end) gload(kt_begin + S - 1);
+        __syncthreads();
+      }
       GroupOps ops[2];
       read_ops(0, kg0, ops[0]);
       // Drain those reads so that both edges into the loop header carry no
@@ -818,7 +860,6 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       // Instruction counts of one iteration, for the interleave below.
       constexpr int N_RD = CB + V * SB;                              // ds_read per group
       constexpr int N_WR = A_LOADS + B_LOADS;                        // ds_write
-      constexpr int N_LD = A_LOADS + B_LOADS;                        // global loads
       constexpr int MPG = V * RB * CB;                                // MFMAs per group
       constexpr bool INTERLEAVE = NGL >= 2 && MPG >= N_WR + N_LD;
       // Operand reads too, one between MFMAs, when a group has room for them.
