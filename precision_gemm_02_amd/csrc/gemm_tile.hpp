@@ -862,6 +862,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       constexpr int N_WR = A_LOADS + B_LOADS;                        // ds_write
       constexpr int MPG = V * RB * CB;                                // MFMAs per group
       constexpr bool INTERLEAVE = NGL >= 2 && MPG >= N_WR + N_LD;
+      // A group too short for both (BK 32 on 32 x 32 wave tiles): the stores
+      // between group 0's MFMAs, the global loads between group 1's.
+      constexpr bool SPLIT = !INTERLEAVE && NGL >= 2 && MPG >= N_WR && MPG >= N_LD;
       // Operand reads too, one between MFMAs, when a group has room for them.
       // After each barrier every wave starts the same group at once; reads
       // issued as a block then queue behind the other waves' reads, and both
@@ -888,7 +891,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       // tile's LDS stores and its global loads are spread evenly between
       // group 0's MFMAs (each executes while an MFMA occupies the matrix
       // core) instead of running as a block while the matrix core idles.
-      const int kt_fast_end = (INTERLEAVE && edge_fast && g.buf32)
+      const int kt_fast_end = ((INTERLEAVE || SPLIT) && edge_fast && g.buf32)
                                   ? max(kt_begin, min(kt_end, k_whole) - S)
                                   : kt_begin;
       // The steady state is unrolled by S, so that every stage index is a
@@ -902,11 +905,22 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         read_ops(st, kg0 + KG, ops[1]);
         if constexpr (!RIL) __builtin_amdgcn_sched_barrier(0);
         lstore(st_store);
-        gload_full(kt + S);
-        // after the tile's own loads, so that waiting for those (in issue
-        // order) never waits for this one
-        if constexpr (QC >= 0) cpf[QC] = load_c_chunk(QC);
+        if constexpr (!SPLIT) {
+          gload_full(kt + S);
+          // after the tile's own loads, so that waiting for those (in issue
+          // order) never waits for this one
+          if constexpr (QC >= 0) cpf[QC] = load_c_chunk(QC);
+        }
         mma(ops[0]);
+        if constexpr (SPLIT) {
+          constexpr int SP = MPG / N_WR;
+  #pragma unroll
+          for (int i = 0; i < N_WR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, MPG - SP * N_WR, 0);
+        }
         if constexpr (INTERLEAVE) {
           // spread evenly: SP MFMAs before each read, store and load
           constexpr int N_LDI = N_LD + ((QC >= 0 && MPG >= N_WR + N_LD + 1) ? 1 : 0);
@@ -937,9 +951,24 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
           // the next tile (kt+1 < kt_fast_end + S <= kt_end) always exists here
           if (gi + 1 < NGL) read_ops(st, kg0 + (gi + 1) * KG, ops[(gi + 1) & 1]);
           else read_ops(st_next, kg0, ops[(gi + 1) & 1]);
-          if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
-          mma(ops[gi & 1]);
-          spread_reads();
+          if (SPLIT && gi == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            gload_full(kt + S);
+            if constexpr (QC >= 0) cpf[QC] = load_c_chunk(QC);
+            mma(ops[gi & 1]);
+            constexpr int N_LDI = N_LD + ((QC >= 0 && MPG >= N_LD + 1) ? 1 : 0);
+            constexpr int SP = MPG / N_LDI;
+  #pragma unroll
+            for (int i = 0; i < N_LDI; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, SP, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MPG - SP * N_LDI, 0);
+          } else {
+            if constexpr (!READS_SPREAD) __builtin_amdgcn_sched_barrier(0);
+            mma(ops[gi & 1]);
+            spread_reads();
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
@@ -961,7 +990,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         mma(ops[0]);
         constexpr int N_WRD = first ? N_WR : 0;
         constexpr int NM = (RIL ? N_RD : 0) + N_WRD;
-        if constexpr (INTERLEAVE && NM > 0) {
+        if constexpr ((INTERLEAVE || SPLIT) && NM > 0) {
           constexpr int SP = MPG / NM;
           if constexpr (RIL) {
   #pragma unroll
