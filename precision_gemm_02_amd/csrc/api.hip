@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -77,6 +78,15 @@ struct TileClass {
   int vec, ua;
   double eff;
   double extra_s;
+  // > 0: this many workgroups share a compute unit and run together; up to
+  // that many tiles per compute unit cost one fixed part and their K loops
+  // (see estimate).
+  int coresident = 0;
+  // Such a class's efficiency with one tile per compute unit and a long K
+  // loop: one wave per SIMD then waits for operands that come from beyond
+  // the L2 (panels that few tiles share, or columns that straddle cache
+  // lines).
+  double eff_lone = 0;
 };
 
 // Variant tables plus the tile classes the shape/alignment choice uses,
@@ -121,13 +131,20 @@ struct Tables {
                find_variant(f32, n32, "f32_64x64x32_w2x2_s3_k2_ua"), 0.96, 1.9e-6};
     // 32 x 32 tiles in four K groups of one wave (one per SIMD), which hand
     // their partial sums over through LDS: problems too small to give every
-    // compute unit a 64 x 64 tile.  Fitted to one round of tiles at 128^3,
-    // 256^3 and 512^3 (4.2, 5.1 and 7.1 us against 5.2, 7.1 and 10.7 for
-    // 64 x 64 tiles): ~0.44 of peak in the K loop (one 32 x 32 block per
-    // wave) and ~1 us more per round; from 768^3 on the 64 x 64 classes
-    // are faster (14.5 against 15.2 us).
+    // compute unit a 64 x 64 tile, and up to three tiles per compute unit
+    // (48 KiB of LDS each), which run together.  Fitted to 19 shapes from
+    // 128^3 to 1024^3 (K up to 4096): ~0.78 of peak in the K loop of one
+    // tile, ~3.6 us fixed in all; 640^3 9.5 us against 11.8 for 64 x 64
+    // tiles, 1024 x 512 x 1024 12.4 against 17.3, but 896^3 22.5 against
+    // 16.2 (four tiles per compute unit: their operand traffic then bounds
+    // them), so beyond three tiles per unit it is priced by rounds.  A lone
+    // tile per unit with a long K loop (8 K tiles or more) runs at 0.5 to
+    // 0.8: 768 x 64 x 2836 22.9 us (panels shared by 2 tiles), 252^2 x 4096
+    // 27.9 (columns of 1008 bytes), 256^2 x 4096 20.1.  It is priced at 0.5,
+    // so that stream-K with 64 x 64 tiles, where a workspace allows it, wins
+    // there (7 of 9 such shapes measured faster with it).
     f32c[5] = {find_variant(f32, n32, "f32_32x32x64_w1x1_s3_k4_vec"),
-               find_variant(f32, n32, "f32_32x32x64_w1x1_s3_k4_ua"), 0.44, 1.0e-6};
+               find_variant(f32, n32, "f32_32x32x64_w1x1_s3_k4_ua"), 0.78, 1.9e-6, 3, 0.5};
     // fp64: 128 x 128 tiles for large problems.  Their 64 x 32 wave tiles
     // leave registers for the unrolled steady-state loop, which more than
     // pays for the extra operand traffic of smaller tiles (4096^3: 74.0
@@ -278,6 +295,11 @@ double estimate(const Variant<T>& v, const TileClass& tc, int m, int n, int k, i
   const long long rounds = tiles / cus, rest = tiles - rounds * cus;
   double kloop, fixed;
   round_costs(v, tc, k, cus, &kloop, &fixed);
+  const long long per_cu = ceil_div(tiles, (long long)cus);
+  if (tc.coresident > 0 && per_cu <= tc.coresident) {
+    const bool lone = per_cu == 1 && k >= 8 * v.bk;
+    return fixed + kloop * (double)per_cu * (lone ? tc.eff / tc.eff_lone : 1.0);
+  }
   const double t = (double)rounds * (kloop + fixed);
   if (rest == 0) return t;
   if (sk != nullptr && sk->wgs > 0)
