@@ -691,11 +691,13 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // last K tiles when beta != 0 and the whole tile lies inside C (pf_c),
     // one chunk per K tile, so that the reads of every tile's C spread over
     // the end of the K loop instead of all arriving in the epilogue at once.
-    // The last chunk waits for the epilogue: one chunk fewer held through the
-    // K loop keeps the 128 x 128 kernel within the 128 registers that leave
-    // room for a second workgroup per compute unit.
+    // The last chunk (two in the kernels with strip workgroups) waits for
+    // the epilogue: fewer chunks held through the K loop keep the 128 x 128
+    // kernel within the 128 registers that leave room for a second workgroup
+    // per compute unit.
     constexpr bool PF_C = Cfg::PF_C && !SKP;
     constexpr int NPF = PF_C ? Cfg::NPF_C : 1;
+    constexpr int NPF_LATE = (STRIPF && NPF > 2) ? 2 : 1;
     chunk_t cpf[NPF];
     const bool pf_c = PF_C && slot < 0 && full_mn && g.beta != T(0);
     bool pf_done = false;
@@ -831,10 +833,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       };
       // The first S-1 tiles whole: all of them in flight at once with tile
       // S-1's register loads (one memory round trip before the first barrier
-      // instead of one per stage).  Not in the kernels with stream-K pieces or
-      // strip workgroups, whose registers it would raise past their
-      // occupancy (or into spills).
-      if (!SKP && !STRIPF && g.buf32 && edge_fast && kt_begin + S - 1 <= min(kt_end, k_whole)) {
+      // instead of one per stage).  Not in the kernels with stream-K pieces,
+      // whose registers it would raise past their occupancy.
+      if (!SKP && g.buf32 && edge_fast && kt_begin + S - 1 <= min(kt_end, k_whole)) {
         for (int t = 0; t < S - 1; ++t) dma_tile(kt_begin + t, t);
         if (kt_begin + S - 1 < kt_end) gload(kt_begin + S - 1);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every stage has landed
@@ -1037,7 +1038,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
               static_for<0, S>([&](auto st_c) {
                 constexpr int q = decltype(trip)::value * S + decltype(st_c)::value;
                 fast_iteration(decltype(st_c)::value, kt + decltype(st_c)::value,
-                               std::integral_constant<int, (q < NPF - 1 ? q : -1)>{});
+                               std::integral_constant<int, (q < NPF - NPF_LATE ? q : -1)>{});
               });
               kt += S;
             });
@@ -1174,7 +1175,10 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   #pragma unroll
           for (int q = 0; q < NPF; ++q) cpf[q] = load_c_chunk(q);
         }
-        if (pre_c && pf_done) cpf[NPF - 1] = load_c_chunk(NPF - 1);   // not prefetched
+        if (pre_c && pf_done) {
+  #pragma unroll
+          for (int q = NPF - NPF_LATE; q < NPF; ++q) cpf[q] = load_c_chunk(q);   // not prefetched
+        }
       } else {
         if (pre_c) load_c_block(0, cpre[0]);
       }
