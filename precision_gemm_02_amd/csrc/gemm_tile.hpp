@@ -833,9 +833,11 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       };
       // The first S-1 tiles whole: all of them in flight at once with tile
       // S-1's register loads (one memory round trip before the first barrier
-      // instead of one per stage).  Not in the kernels with stream-K pieces,
-      // whose registers it would raise past their occupancy.
-      if (!SKP && g.buf32 && edge_fast && kt_begin + S - 1 <= min(kt_end, k_whole)) {
+      // instead of one per stage).  Of the kernels with stream-K pieces only
+      // the fp32 128 x 128 one: in the 64 x 64 ones it raises the registers
+      // past their occupancy, and in fp64 it measured no gain.
+      constexpr bool PRO_DMA = !SKP || (BM >= 128 && sizeof(T) == 4);
+      if (PRO_DMA && g.buf32 && edge_fast && kt_begin + S - 1 <= min(kt_end, k_whole)) {
         for (int t = 0; t < S - 1; ++t) dma_tile(kt_begin + t, t);
         if (kt_begin + S - 1 < kt_end) gload(kt_begin + S - 1);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every stage has landed
