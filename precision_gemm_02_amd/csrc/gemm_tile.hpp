@@ -691,13 +691,13 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // last K tiles when beta != 0 and the whole tile lies inside C (pf_c),
     // one chunk per K tile, so that the reads of every tile's C spread over
     // the end of the K loop instead of all arriving in the epilogue at once.
-    // The last chunk (two in the kernels with strip workgroups) waits for
-    // the epilogue: fewer chunks held through the K loop keep the 128 x 128
-    // kernel within the 128 registers that leave room for a second workgroup
-    // per compute unit.
+    // The last chunk (three in the kernels with strip workgroups, which also
+    // hold the strip role's registers) waits for the epilogue: fewer chunks
+    // held through the K loop keep the 128 x 128 kernel within the 128
+    // registers that leave room for a second workgroup per compute unit.
     constexpr bool PF_C = Cfg::PF_C && !SKP;
     constexpr int NPF = PF_C ? Cfg::NPF_C : 1;
-    constexpr int NPF_LATE = (STRIPF && NPF > 2) ? 2 : 1;
+    constexpr int NPF_LATE = (STRIPF && NPF > 3) ? 3 : 1;
     chunk_t cpf[NPF];
     const bool pf_c = PF_C && slot < 0 && full_mn && g.beta != T(0);
     bool pf_done = false;
@@ -1052,9 +1052,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         fast_iteration(st, kt, NoC{});
         st = (st + 1 == S) ? 0 : st + 1;
       }
-      // (Not in the kernels with strip workgroups: its registers would cost
-      // their tiles more spills than the drain saves.)
-      if constexpr (Cfg::UNROLL && !STRIPF) {
+      if constexpr (Cfg::UNROLL) {
         if (st == 0 && kt == kt_fast_end && kt + S == kt_end && kt > kt_begin) {
           static_for<0, S>([&](auto st_c) { drain_iteration(st_c); });
           kt = kt_end;
