@@ -134,6 +134,20 @@ def test_selection_by_shape_and_alignment():
     assert name_of(v) == "f32_64x64x32_w2x2_s3_k2_vec"
     v = pg.select_f32(1024, 1024, 8192, 1.0, FAKE_ODD, 1024, FAKE, 8192, 0.0, FAKE, 1024)
     assert name_of(v) == "f32_64x64x32_w2x2_s3_k2_ua"
+    # 32 x 32 tiles in four K groups: small problems, and up to three tiles
+    # per compute unit, which run together (640^3: 400 tiles; 768^3: 576);
+    # four or more per unit are priced by rounds (896^3: 784 tiles)
+    for n in (128, 512, 640, 768):
+        v = pg.select_f32(n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)
+        assert name_of(v) == "f32_32x32x64_w1x1_s3_k4_vec", (n, name_of(v))
+    v = pg.select_f32(896, 896, 896, 1.0, FAKE, 896, FAKE, 896, 0.0, FAKE, 896)
+    assert name_of(v) == "f32_64x64x16_w2x2_s4_vec"
+    # one such tile per unit with a long K loop is priced low enough that
+    # stream-K of 64 x 64 tiles takes it where a workspace allows
+    e = (732, 316, 3260, 1.0, FAKE, 732, FAKE, 3260, 0.0, FAKE, 732)
+    assert name_of(pg.select_f32(*e)) == "f32_32x32x64_w1x1_s3_k4_vec"
+    v, sk, _ = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
+    assert name_of(v) == "f32_64x64x16_w2x2_s4_vec" and sk > 0
     # odd leading dimensions select the unaligned path
     v = pg.select_f32(4097, 3001, 1023, 0.75, FAKE, 4113, FAKE, 1039, -1.25, FAKE, 4113)
     assert name_of(v).endswith("_ua")
