@@ -691,13 +691,14 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // last K tiles when beta != 0 and the whole tile lies inside C (pf_c),
     // one chunk per K tile, so that the reads of every tile's C spread over
     // the end of the K loop instead of all arriving in the epilogue at once.
-    // The last chunk (three in the kernels with strip workgroups, which also
-    // hold the strip role's registers) waits for the epilogue: fewer chunks
-    // held through the K loop keep the 128 x 128 kernel within the 128
-    // registers that leave room for a second workgroup per compute unit.
+    // The last chunk (three in the 128 x 128 kernel with strip workgroups,
+    // which also holds the strip role's registers) waits for the epilogue:
+    // fewer chunks held through the K loop keep the 128 x 128 kernels within
+    // the 128 registers that leave room for a second workgroup per compute
+    // unit.
     constexpr bool PF_C = Cfg::PF_C && !SKP;
     constexpr int NPF = PF_C ? Cfg::NPF_C : 1;
-    constexpr int NPF_LATE = (STRIPF && NPF > 3) ? 3 : 1;
+    constexpr int NPF_LATE = (STRIPF && BM >= 128 && NPF > 3) ? 3 : 1;
     chunk_t cpf[NPF];
     const bool pf_c = PF_C && slot < 0 && full_mn && g.beta != T(0);
     bool pf_done = false;
