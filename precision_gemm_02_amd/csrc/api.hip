@@ -131,19 +131,19 @@ struct Tables {
     // 32 x 32 tiles in four K groups of one wave (one per SIMD), which hand
     // their partial sums over through LDS: problems too small to give every
     // compute unit a 64 x 64 tile, and up to three tiles per compute unit
-    // (48 KiB of LDS each), which run together.  Fitted to 19 shapes from
-    // 128^3 to 1024^3 (K up to 4096): ~0.78 of peak in the K loop of one
-    // tile, ~3.6 us fixed in all; 640^3 9.5 us against 11.8 for 64 x 64
-    // tiles, 1024 x 512 x 1024 12.4 against 17.3, but 896^3 22.5 against
-    // 16.2 (four tiles per compute unit: their operand traffic then bounds
-    // them), so beyond three tiles per unit it is priced by rounds.  A lone
+    // (48 KiB of LDS each), which run together.  Fitted to 23 shapes from
+    // 128^3 to 1536 x 512 x 256 (K up to 4096): ~0.80 of peak in the K loop
+    // of one tile, ~3.5 us fixed in all; 640^3 8.7 us against 11.9 for
+    // 64 x 64 tiles, 1024 x 512 x 1024 11.7 against 17.3, but 1024^3 24.0
+    // against 17.8 (four tiles per compute unit: their operand traffic then
+    // bounds them), so beyond three tiles per unit it is priced by rounds.  A lone
     // tile per unit with a long K loop (8 K tiles or more) runs at 0.5 to
     // 0.8: 768 x 64 x 2836 22.9 us (panels shared by 2 tiles), 252^2 x 4096
     // 27.9 (columns of 1008 bytes), 256^2 x 4096 20.1.  It is priced at 0.5,
     // so that stream-K with 64 x 64 tiles, where a workspace allows it, wins
     // there (7 of 9 such shapes measured faster with it).
     f32c[5] = {find_variant(f32, n32, "f32_32x32x64_w1x1_s3_k4_vec"),
-               find_variant(f32, n32, "f32_32x32x64_w1x1_s3_k4_ua"), 0.78, 1.9e-6, 3, 0.5};
+               find_variant(f32, n32, "f32_32x32x64_w1x1_s3_k4_ua"), 0.80, 1.75e-6, 3, 0.5};
     // fp64: 128 x 128 tiles for large problems.  Their 64 x 32 wave tiles
     // leave registers for the unrolled steady-state loop, which more than
     // pays for the extra operand traffic of smaller tiles (4096^3: 74.0

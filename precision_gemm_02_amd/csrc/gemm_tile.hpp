@@ -1083,6 +1083,82 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       }
     }
 
+    // K groups of one wave each (the 32 x 32 class): every group stages its
+    // partial sums in an LDS region of its own, in the staged epilogue's
+    // layout, and then every wave takes a quarter of the tile's chunks, adds
+    // the groups' values in group order (the same sums as a hand-over to
+    // group 0) and stores them: no serial hand-over and staging by group 0.
+    constexpr bool PAR_EPI = KS > 1 && WGM * WGN == 1 && CB == 1 && Cfg::STAGED_EPI && !SKP;
+    if constexpr (PAR_EPI) {
+      constexpr int LDW = Cfg::EPI_LDW;            // staging column stride (elements)
+      constexpr int CPC = Cfg::WM / V;             // chunks per column
+      constexpr int NCH = MB * CPC;                // chunks of the tile
+      constexpr int RUN_E = TR::RUN_R * W, NRUN_E = TR::NACC / TR::RUN_R;
+      static_assert(NCH == KS * 64, "one chunk per lane of the workgroup");
+      static_assert(KS * MB * LDW <= Cfg::LDS_ELEMS, "a staging region per group");
+      const int q = lane + 64 * kgrp;
+      const int col = q / CPC, rc = q % CPC;
+      const int gcol = n0 + col, grow = m0 + rc * V;
+      const T alpha = g.alpha, beta = g.beta;
+      const bool read_c = beta != T(0);
+      T* const pc = g.C + (size_t)gcol * g.ldc + grow;
+      chunk_t cold{};
+      if (read_c && full_mn) cold = load_chunk_full<TR, VEC>(pc);
+      __syncthreads();                       // every wave is done with the ring
+      T* const stg = lds + kgrp * (MB * LDW);
+  #pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+  #pragma unroll
+        for (int run = 0; run < NRUN_E; ++run) {
+          T* const pcol = stg + lrow * LDW;
+          const int ch0 = (sb * MB * W + W * TR::irow(run, kslot)) / V;
+  #pragma unroll
+          for (int h = 0; h < RUN_E / V; ++h) {
+            chunk_t v;
+  #pragma unroll
+            for (int e = 0; e < V; ++e) {
+              const int o = h * V + e;
+              v[e] = acc[sb * W + o % W][0][run * TR::RUN_R + o / W];
+            }
+            *reinterpret_cast<chunk_t*>(pcol + ((ch0 + h) ^ (lrow & 7)) * V) = v;
+          }
+        }
+      }
+      __syncthreads();
+      chunk_t v = *reinterpret_cast<const chunk_t*>(lds + col * LDW + (rc ^ (col & 7)) * V);
+  #pragma unroll
+      for (int j = 1; j < KS; ++j) {
+        const chunk_t p =
+            *reinterpret_cast<const chunk_t*>(lds + j * (MB * LDW) + col * LDW + (rc ^ (col & 7)) * V);
+  #pragma unroll
+        for (int e = 0; e < V; ++e) v[e] += p[e];
+      }
+      if (gcol < N) {
+        if (grow + V <= M) {
+          chunk_t out;
+          if (read_c) {
+            if (!full_mn) cold = load_chunk_full<TR, VEC>(pc);
+  #pragma unroll
+            for (int e = 0; e < V; ++e) out[e] = fma_t(beta, cold[e], alpha * v[e]);
+          } else {
+  #pragma unroll
+            for (int e = 0; e < V; ++e) out[e] = alpha * v[e];
+          }
+          store_chunk<TR, VEC>(pc, out);
+        } else {
+  #pragma unroll
+          for (int e = 0; e < V; ++e) {
+            if (grow + e < M) {
+              T o = alpha * v[e];
+              if (read_c) o = fma_t(beta, pc[e], o);
+              pc[e] = o;
+            }
+          }
+        }
+      }
+      return;
+    }
+
     if constexpr (KS > 1) {
       // Groups 1 .. KS-1 hand their partial sums to group 0 through LDS
       // (lane-linear, so each register index is one contiguous 256-byte row
