@@ -1083,29 +1083,41 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       }
     }
 
-    // K groups of one wave each (the 32 x 32 class): every group stages its
-    // partial sums in an LDS region of its own, in the staged epilogue's
-    // layout, and then every wave takes a quarter of the tile's chunks, adds
-    // the groups' values in group order (the same sums as a hand-over to
-    // group 0) and stores them: no serial hand-over and staging by group 0.
-    constexpr bool PAR_EPI = KS > 1 && WGM * WGN == 1 && CB == 1 && Cfg::STAGED_EPI && !SKP;
+    // K groups with one column block per wave: every wave stages its partial
+    // sums in an LDS region of its own (group g, wave w), in the staged
+    // epilogue's layout, and then every thread takes its share of the tile's
+    // 16-byte chunks, adds the groups' values in group order (the same sums
+    // as a hand-over to group 0) and stores them: no serial hand-over, and no
+    // staging by group 0 alone while the other groups wait.
+    constexpr bool PAR_EPI = KS > 1 && CB == 1 && Cfg::STAGED_EPI && !SKP;
     if constexpr (PAR_EPI) {
+      constexpr int NW = WGM * WGN;                // waves per group
       constexpr int LDW = Cfg::EPI_LDW;            // staging column stride (elements)
-      constexpr int CPC = Cfg::WM / V;             // chunks per column
-      constexpr int NCH = MB * CPC;                // chunks of the tile
+      constexpr int CPC = Cfg::WM / V;             // chunks per wave-tile column
+      constexpr int WCH = MB * CPC;                // chunks per wave tile
+      constexpr int PER = NW * WCH / NT;           // chunks per thread
       constexpr int RUN_E = TR::RUN_R * W, NRUN_E = TR::NACC / TR::RUN_R;
-      static_assert(NCH == KS * 64, "one chunk per lane of the workgroup");
-      static_assert(KS * MB * LDW <= Cfg::LDS_ELEMS, "a staging region per group");
-      const int q = lane + 64 * kgrp;
-      const int col = q / CPC, rc = q % CPC;
-      const int gcol = n0 + col, grow = m0 + rc * V;
+      static_assert(PER >= 1 && NW * WCH == PER * NT, "whole chunks per thread");
+      static_assert(KS * NW * MB * LDW <= Cfg::LDS_ELEMS, "a staging region per wave");
       const T alpha = g.alpha, beta = g.beta;
       const bool read_c = beta != T(0);
-      T* const pc = g.C + (size_t)gcol * g.ldc + grow;
-      chunk_t cold{};
-      if (read_c && full_mn) cold = load_chunk_full<TR, VEC>(pc);
+      // this thread's chunks: wave tile w, column col, rows rc*V .. rc*V+V-1
+      int gcol[PER], grow[PER], loff[PER];
+      chunk_t cold[PER];
+  #pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int q = tid + i * NT;
+        const int w = q / WCH, qq = q % WCH;
+        const int col = qq / CPC, rc = qq % CPC;
+        gcol[i] = n0 + (w / WGM) * Cfg::WN + col;
+        grow[i] = m0 + (w % WGM) * Cfg::WM + rc * V;
+        loff[i] = w * (MB * LDW) + col * LDW + (rc ^ (col & 7)) * V;
+        cold[i] = chunk_t{};
+        if (read_c && full_mn)
+          cold[i] = load_chunk_full<TR, VEC>(g.C + (size_t)gcol[i] * g.ldc + grow[i]);
+      }
       __syncthreads();                       // every wave is done with the ring
-      T* const stg = lds + kgrp * (MB * LDW);
+      T* const stg = lds + (kgrp * NW + wave_in) * (MB * LDW);
   #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
   #pragma unroll
@@ -1125,21 +1137,23 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         }
       }
       __syncthreads();
-      chunk_t v = *reinterpret_cast<const chunk_t*>(lds + col * LDW + (rc ^ (col & 7)) * V);
   #pragma unroll
-      for (int j = 1; j < KS; ++j) {
-        const chunk_t p =
-            *reinterpret_cast<const chunk_t*>(lds + j * (MB * LDW) + col * LDW + (rc ^ (col & 7)) * V);
+      for (int i = 0; i < PER; ++i) {
+        chunk_t v = *reinterpret_cast<const chunk_t*>(lds + loff[i]);
   #pragma unroll
-        for (int e = 0; e < V; ++e) v[e] += p[e];
-      }
-      if (gcol < N) {
-        if (grow + V <= M) {
+        for (int j = 1; j < KS; ++j) {
+          const chunk_t p = *reinterpret_cast<const chunk_t*>(lds + j * (NW * MB * LDW) + loff[i]);
+  #pragma unroll
+          for (int e = 0; e < V; ++e) v[e] += p[e];
+        }
+        if (gcol[i] >= N) continue;
+        T* const pc = g.C + (size_t)gcol[i] * g.ldc + grow[i];
+        if (grow[i] + V <= M) {
           chunk_t out;
           if (read_c) {
-            if (!full_mn) cold = load_chunk_full<TR, VEC>(pc);
+            if (!full_mn) cold[i] = load_chunk_full<TR, VEC>(pc);
   #pragma unroll
-            for (int e = 0; e < V; ++e) out[e] = fma_t(beta, cold[e], alpha * v[e]);
+            for (int e = 0; e < V; ++e) out[e] = fma_t(beta, cold[i][e], alpha * v[e]);
           } else {
   #pragma unroll
             for (int e = 0; e < V; ++e) out[e] = alpha * v[e];
@@ -1148,7 +1162,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         } else {
   #pragma unroll
           for (int e = 0; e < V; ++e) {
-            if (grow + e < M) {
+            if (grow[i] + e < M) {
               T o = alpha * v[e];
               if (read_c) o = fma_t(beta, pc[e], o);
               pc[e] = o;
