@@ -1089,7 +1089,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     // 16-byte chunks, adds the groups' values in group order (the same sums
     // as a hand-over to group 0) and stores them: no serial hand-over, and no
     // staging by group 0 alone while the other groups wait.
-    constexpr bool PAR_EPI = KS > 1 && CB == 1 && Cfg::STAGED_EPI && !SKP;
+    constexpr bool PAR_EPI = KS > 1 && CB == 1 && Cfg::STAGED_EPI;
     if constexpr (PAR_EPI) {
       constexpr int NW = WGM * WGN;                // waves per group
       constexpr int LDW = Cfg::EPI_LDW;            // staging column stride (elements)
@@ -1099,7 +1099,15 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       constexpr int RUN_E = TR::RUN_R * W, NRUN_E = TR::NACC / TR::RUN_R;
       static_assert(PER >= 1 && NW * WCH == PER * NT, "whole chunks per thread");
       static_assert(KS * NW * MB * LDW <= Cfg::LDS_ELEMS, "a staging region per wave");
-      const T alpha = g.alpha, beta = g.beta;
+      // Destination: C, or for a stream-K piece its raw partial sums (alpha
+      // = 1, beta = 0, all BM x BN elements, column-major with ld = BM) in
+      // workspace slot `slot`.
+      const bool to_ws = slot >= 0;
+      T* const cbase = to_ws ? g.ws + (size_t)slot * (BM * BN) : g.C;
+      const int ldc = to_ws ? BM : g.ldc;
+      const int m_end = to_ws ? BM : M, n_end = to_ws ? BN : N;
+      const int r0 = to_ws ? 0 : m0, c0 = to_ws ? 0 : n0;
+      const T alpha = to_ws ? T(1) : g.alpha, beta = to_ws ? T(0) : g.beta;
       const bool read_c = beta != T(0);
       // this thread's chunks: wave tile w, column col, rows rc*V .. rc*V+V-1
       int gcol[PER], grow[PER], loff[PER];
@@ -1109,12 +1117,12 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         const int q = tid + i * NT;
         const int w = q / WCH, qq = q % WCH;
         const int col = qq / CPC, rc = qq % CPC;
-        gcol[i] = n0 + (w / WGM) * Cfg::WN + col;
-        grow[i] = m0 + (w % WGM) * Cfg::WM + rc * V;
+        gcol[i] = c0 + (w / WGM) * Cfg::WN + col;
+        grow[i] = r0 + (w % WGM) * Cfg::WM + rc * V;
         loff[i] = w * (MB * LDW) + col * LDW + (rc ^ (col & 7)) * V;
         cold[i] = chunk_t{};
         if (read_c && full_mn)
-          cold[i] = load_chunk_full<TR, VEC>(g.C + (size_t)gcol[i] * g.ldc + grow[i]);
+          cold[i] = load_chunk_full<TR, VEC>(cbase + (size_t)gcol[i] * ldc + grow[i]);
       }
       __syncthreads();                       // every wave is done with the ring
       T* const stg = lds + (kgrp * NW + wave_in) * (MB * LDW);
@@ -1146,9 +1154,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   #pragma unroll
           for (int e = 0; e < V; ++e) v[e] += p[e];
         }
-        if (gcol[i] >= N) continue;
-        T* const pc = g.C + (size_t)gcol[i] * g.ldc + grow[i];
-        if (grow[i] + V <= M) {
+        if (gcol[i] >= n_end) continue;
+        T* const pc = cbase + (size_t)gcol[i] * ldc + grow[i];
+        if (grow[i] + V <= m_end) {
           chunk_t out;
           if (read_c) {
             if (!full_mn) cold[i] = load_chunk_full<TR, VEC>(pc);
@@ -1162,7 +1170,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         } else {
   #pragma unroll
           for (int e = 0; e < V; ++e) {
-            if (grow[i] + e < M) {
+            if (grow[i] + e < m_end) {
               T o = alpha * v[e];
               if (read_c) o = fma_t(beta, pc[e], o);
               pc[e] = o;
