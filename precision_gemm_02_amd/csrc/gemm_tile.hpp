@@ -214,6 +214,12 @@ struct TileCfg {
   // K tiles over which those loads are spread: whole trips of the unrolled
   // steady state
   static constexpr int PF_ITERS = (NPF_C + STAGES - 1) / STAGES * STAGES;
+  // Direct-store epilogue with beta != 0: the tile's whole old C (one
+  // element per accumulator, in the accumulators' layout) can be loaded into
+  // registers once the K loop has issued its last global loads, when that
+  // takes at most 64 registers.
+  static constexpr bool PF_CT =
+      !STAGED_EPI && KS == 1 && RB * CB * TR::NACC * (int)sizeof(T) / 4 <= 64;
   // When the grid also computes strip rows (one K group per strip
   // workgroup: its latency passes beside the tiles), the strip role's sums
   // per thread (at most STRIP_ACC elements, STRIP_SCMAX columns per wave)
@@ -702,6 +708,21 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     chunk_t cpf[NPF];
     const bool pf_c = PF_C && slot < 0 && full_mn && g.beta != T(0);
     bool pf_done = false;
+    // A lane's accumulator registers come in runs of RUN_R consecutive block
+    // rows (see the trait).  Block b = sb*W + b' puts block row i at wave-tile
+    // row sb*MB*W + W*i + b', so for fixed (c, sb, run) the lane owns RUN =
+    // RUN_R*W consecutive rows of one column: element o of that run is
+    // register run*RUN_R + o/W of block sb*W + o%W.
+    constexpr int RUN = TR::RUN_R * W;
+    constexpr int NRUN = TR::NACC / TR::RUN_R;
+    // Direct-store epilogue: the old C of this lane's runs for group
+    // gq = c*SB + sb, all of it loaded during the last K tiles (which read
+    // only LDS) when beta != 0 and the whole tile lies inside C (ct_c).
+    constexpr bool PF_CT = Cfg::PF_CT && !SKP;
+    constexpr int NCT = PF_CT ? CB * SB : 1;
+    T ct[NCT][NRUN][RUN];
+    const bool ct_c = PF_CT && slot < 0 && full_mn && g.beta != T(0);
+    bool ct_done = false;
     auto load_c_chunk = [&](const int q) __attribute__((always_inline)) {
       const int c = q / Cfg::EPI_NI, qq = lane + 64 * (q % Cfg::EPI_NI);
       const int col = qq / Cfg::EPI_CPC, rc = qq % Cfg::EPI_CPC;
@@ -1059,6 +1080,37 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
           kt = kt_end;
         }
       }
+      // Old C for the direct-store epilogue, when at most the last S tiles
+      // remain: they issue no global loads, and their LDS reads and MFMAs
+      // (thousands of cycles per tile) hide the loads' latency.  Issued after
+      // the last tile's own loads, so that waiting for those (in issue order)
+      // never waits for these.
+      if constexpr (PF_CT) {
+        if (ct_c && kt_end - kt <= S) {
+          static_for<0, NCT>([&](auto gq_c) {
+            constexpr int gq = decltype(gq_c)::value;
+            constexpr int c = gq / SB, sb = gq % SB;
+            const T* pcol = g.C + (size_t)(n0 + wcol + c * MB + lrow) * g.ldc;
+            const int row0 = m0 + wrow + sb * MB * W;
+  #pragma unroll
+            for (int run = 0; run < NRUN; ++run) {
+              const T* pc = pcol + row0 + W * TR::irow(run, kslot);
+              if constexpr (RUN % V == 0) {
+  #pragma unroll
+                for (int h = 0; h < RUN / V; ++h) {
+                  chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
+  #pragma unroll
+                  for (int e = 0; e < V; ++e) ct[gq][run][h * V + e] = v[e];
+                }
+              } else {
+  #pragma unroll
+                for (int o = 0; o < RUN; ++o) ct[gq][run][o] = pc[o];
+              }
+            }
+          });
+          ct_done = true;
+        }
+      }
       // Remaining iterations (edge tiles, the K tail, the last S tiles).
       for (; kt < kt_end; ++kt) {
         const int st_next = (st + 1 == S) ? 0 : st + 1;
@@ -1224,13 +1276,6 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
     const int ldc = to_ws ? BM : g.ldc;
     const T alpha = to_ws ? T(1) : g.alpha, beta = to_ws ? T(0) : g.beta;
     const bool read_c = beta != T(0);
-    constexpr int RUN = TR::RUN_R * W;
-    constexpr int NRUN = TR::NACC / TR::RUN_R;
-    // A lane's accumulator registers come in runs of RUN_R consecutive block
-    // rows (see the trait).  Block b = sb*W + b' puts block row i at wave-tile
-    // row sb*MB*W + W*i + b', so for fixed (c, sb, run) the lane owns RUN =
-    // RUN_R*W consecutive rows of one column: element o of that run is
-    // register run*RUN_R + o/W of block sb*W + o%W.
     if constexpr (Cfg::STAGED_EPI) {
       // Staged through LDS so that global memory sees whole column segments.
       // Per column block c, each wave writes its MB columns x WM rows to a
@@ -1384,16 +1429,9 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         }
       };
       if (read_c && full_mn && !to_ws) {
-        // Whole tile inside C with beta != 0: the old C of the next group is
-        // loaded before this group's multiply-adds and stores, so that one
-        // HBM latency is exposed per tile instead of one per group.
-        constexpr int NG_EPI = CB * SB;
-        T cvb[2][NRUN][RUN];
-        load_c_group(0, 0, cvb[0]);
-  #pragma unroll
-        for (int gq = 0; gq < NG_EPI; ++gq) {
-          const int c = gq / SB, sb = gq % SB;
-          if (gq + 1 < NG_EPI) load_c_group((gq + 1) / SB, (gq + 1) % SB, cvb[(gq + 1) & 1]);
+        // Whole tile inside C with beta != 0.
+        auto put_group = [&](const int c, const int sb, const T (&cv)[NRUN][RUN])
+                             __attribute__((always_inline)) {
           T* pcol = cbase + (size_t)(col_off + wcol + c * MB + lrow) * ldc;
           const int row0 = row_off + wrow + sb * MB * W;
   #pragma unroll
@@ -1402,8 +1440,8 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
             T out[RUN];
   #pragma unroll
             for (int o = 0; o < RUN; ++o)
-              out[o] = fma_t(beta, cvb[gq & 1][run][o],
-                                     alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W]);
+              out[o] = fma_t(beta, cv[run][o],
+                             alpha * acc[sb * W + o % W][c][run * TR::RUN_R + o / W]);
             if constexpr (VEC_C) {
   #pragma unroll
               for (int h = 0; h < RUN / V; ++h) {
@@ -1417,6 +1455,25 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
               for (int o = 0; o < RUN; ++o) pc[o] = out[o];
             }
           }
+        };
+        constexpr int NG_EPI = CB * SB;
+        if constexpr (PF_CT) {
+          if (ct_done) {
+            // loaded during the last K tiles
+  #pragma unroll
+            for (int gq = 0; gq < NG_EPI; ++gq) put_group(gq / SB, gq % SB, ct[gq]);
+            return;
+          }
+        }
+        // Otherwise the old C of the next group is loaded before this group's
+        // multiply-adds and stores, so that one HBM latency is exposed per
+        // tile instead of one per group.
+        T cvb[2][NRUN][RUN];
+        load_c_group(0, 0, cvb[0]);
+  #pragma unroll
+        for (int gq = 0; gq < NG_EPI; ++gq) {
+          if (gq + 1 < NG_EPI) load_c_group((gq + 1) / SB, (gq + 1) % SB, cvb[(gq + 1) & 1]);
+          put_group(gq / SB, gq % SB, cvb[gq & 1]);
         }
         return;
       }
