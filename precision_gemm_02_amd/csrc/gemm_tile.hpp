@@ -998,6 +998,39 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         }
         __syncthreads();
       };
+      // Old C for the direct-store epilogue (ct_c), issued by the second of
+      // the last S tiles (in the drain below or the loop after it): the first
+      // one's LDS stores have consumed every A and B load by then, so no wait
+      // for those can also wait for these, and the remaining tiles (LDS reads
+      // and MFMAs only, thousands of cycles each) hide their latency.
+      auto load_ct = [&]() __attribute__((always_inline)) {
+        if constexpr (PF_CT) {
+          if (ct_c) {
+            static_for<0, NCT>([&](auto gq_c) {
+              constexpr int gq = decltype(gq_c)::value;
+              constexpr int c = gq / SB, sb = gq % SB;
+              const T* pcol = g.C + (size_t)(n0 + wcol + c * MB + lrow) * g.ldc;
+              const int row0 = m0 + wrow + sb * MB * W;
+  #pragma unroll
+              for (int run = 0; run < NRUN; ++run) {
+                const T* pc = pcol + row0 + W * TR::irow(run, kslot);
+                if constexpr (RUN % V == 0) {
+  #pragma unroll
+                  for (int h = 0; h < RUN / V; ++h) {
+                    chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
+  #pragma unroll
+                    for (int e = 0; e < V; ++e) ct[gq][run][h * V + e] = v[e];
+                  }
+                } else {
+  #pragma unroll
+                  for (int o = 0; o < RUN; ++o) ct[gq][run][o] = pc[o];
+                }
+              }
+            });
+            ct_done = true;
+          }
+        }
+      };
       // The last S tiles when they are whole and the steady state ends at
       // stage 0 (K a multiple of S*BK on the fast path): the same iteration
       // without global loads, the first storing the last tile fetched, and
@@ -1009,6 +1042,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
         constexpr bool first = st == 0, last = st == S - 1;
         // the last tile's prefetch re-reads its own stage (in bounds, unused)
         constexpr int st_next = last ? st : st + 1;
+        if constexpr (st == 1) load_ct();
         read_ops(st, kg0 + KG, ops[1]);
         if constexpr (!RIL) __builtin_amdgcn_sched_barrier(0);
         if constexpr (first) lstore(S - 1);
@@ -1080,39 +1114,11 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
           kt = kt_end;
         }
       }
-      // Old C for the direct-store epilogue, when at most the last S tiles
-      // remain: they issue no global loads, and their LDS reads and MFMAs
-      // (thousands of cycles per tile) hide the loads' latency.  Issued after
-      // the last tile's own loads, so that waiting for those (in issue order)
-      // never waits for these.
-      if constexpr (PF_CT) {
-        if (ct_c && kt_end - kt <= S) {
-          static_for<0, NCT>([&](auto gq_c) {
-            constexpr int gq = decltype(gq_c)::value;
-            constexpr int c = gq / SB, sb = gq % SB;
-            const T* pcol = g.C + (size_t)(n0 + wcol + c * MB + lrow) * g.ldc;
-            const int row0 = m0 + wrow + sb * MB * W;
-  #pragma unroll
-            for (int run = 0; run < NRUN; ++run) {
-              const T* pc = pcol + row0 + W * TR::irow(run, kslot);
-              if constexpr (RUN % V == 0) {
-  #pragma unroll
-                for (int h = 0; h < RUN / V; ++h) {
-                  chunk_t v = load_chunk_full<TR, VEC>(pc + h * V);
-  #pragma unroll
-                  for (int e = 0; e < V; ++e) ct[gq][run][h * V + e] = v[e];
-                }
-              } else {
-  #pragma unroll
-                for (int o = 0; o < RUN; ++o) ct[gq][run][o] = pc[o];
-              }
-            }
-          });
-          ct_done = true;
-        }
-      }
       // Remaining iterations (edge tiles, the K tail, the last S tiles).
       for (; kt < kt_end; ++kt) {
+        if constexpr (PF_CT) {
+          if (kt == kt_end - S + 1) load_ct();
+        }
         const int st_next = (st + 1 == S) ? 0 : st + 1;
         const int st_store = (st == 0) ? S - 1 : st - 1;   // (kt + S - 1) % S
         // At the last tile the prefetch re-reads this tile's own stage (in
