@@ -224,6 +224,36 @@ def test_ring_pipeline_boundaries(variant):
             t += 1
 
 
+@pytest.mark.parametrize("variant", [v for v in ring_variants()
+                                     if pg.variants()[v].startswith("f64_")],
+                         ids=lambda v: pg.variants()[v])
+def test_f64_old_c_loaded_in_last_k_tiles(variant):
+    """The fp64 kernels load a whole tile's old C during the last K tiles when
+    beta != 0 and the tile lies inside C: in the compile-time drain when the
+    steady state ends at stage 0 (K = 2*S*BK), in the loop over the last
+    tiles otherwise (K = (2S+1)*BK, and with a K tail).  Every alpha/beta
+    pair, whole and edge tiles; with beta = 0, C holds NaN and is never read."""
+    name = pg.variants()[variant]
+    m = re.match(r"f64_(\d+)x(\d+)x(\d+)_w\d+x\d+_s(\d+)_(vec|ua)$", name)
+    BM, BN, BK, S, kind = (int(m.group(1)), int(m.group(2)), int(m.group(3)),
+                           int(m.group(4)), m.group(5))
+    t = 0
+    for (mm, nn) in [(2 * BM, 2 * BN), (2 * BM + 3, BN + 5)]:
+        for k in (BK * 2 * S, BK * (2 * S + 1), BK * (2 * S + 1) + 3):
+            for alpha, beta in ALPHA_BETA:
+                lds = leading_dims(mm, k, kind == "vec", 2, t)
+                p = exact_problem(np.float64, mm, nn, k, alpha, beta, lds, seed=900 + t)
+                if beta == 0:
+                    p.C = gi.colmajor(np.full(mm * nn, np.nan), mm, nn, p.ldc,
+                                      gi.C_SENTINEL_F64)
+                say(name, (mm, nn, k), (alpha, beta), "ld", lds)
+                C, _ = run_colmajor(p, variant=variant)
+                assert_bitwise(C, oracle_full(p))
+                if beta == 0:
+                    assert not np.isnan(C).any()
+                t += 1
+
+
 @pytest.mark.parametrize("name", ["sgemm_128", "sgemm_2048", "sgemm_sweep_4096",
                                   "sgemm_ragged"])
 def test_workload_shapes_exact_integer(name):
