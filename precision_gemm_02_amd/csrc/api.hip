@@ -363,7 +363,7 @@ struct Choice {
 // sk_ok (only where that is estimated at least 1 % faster: below that the
 // measured gains were within noise or losses).
 template <typename T>
-Choice choose(int m, int n, int k, bool sk_ok) {
+Choice choose(int m, int n, int k, bool sk_ok, long long ldc) {
   const Tables& t = tables();
   const Variant<T>* table;
   const TileClass* cls;
@@ -383,6 +383,7 @@ Choice choose(int m, int n, int k, bool sk_ok) {
   double best_t = -1;
   for (int c = 0; c < ncls; ++c) {
     const Variant<T>& v = table[cls[c].vec];
+    if (v.max_ldc > 0 && ldc > v.max_ldc) continue;   // C's offsets would not fit
     const int r = strip_rows(v, m);
     double e_cls = 0;
     for (int o = 0; o < (r > 0 ? 2 : 1); ++o) {
@@ -420,20 +421,20 @@ Choice choose(int m, int n, int k, bool sk_ok) {
 // workspace large enough for the plan of the choice that is best with
 // stream-K, that choice; otherwise the best one without stream-K.
 template <typename T>
-int pick(int m, int n, int k, bool vec, size_t ws_bytes, SkPlan* plan, int* strip) {
+int pick(int m, int n, int k, int ldc, bool vec, size_t ws_bytes, SkPlan* plan, int* strip) {
   const Tables& t = tables();
   const TileClass* cls;
   if constexpr (sizeof(T) == 4) cls = t.f32c;
   else cls = t.f64c;
   if (ws_bytes > 0) {
-    const Choice c = choose<T>(m, n, k, true);
+    const Choice c = choose<T>(m, n, k, true, ldc);
     if (c.plan.wgs == 0 || ws_bytes >= c.plan.bytes) {
       *plan = c.plan;
       *strip = c.strip;
       return vec ? cls[c.cls].vec : cls[c.cls].ua;
     }
   }
-  const Choice c = choose<T>(m, n, k, false);
+  const Choice c = choose<T>(m, n, k, false, ldc);
   *plan = SkPlan{};
   *strip = c.strip;
   return vec ? cls[c.cls].vec : cls[c.cls].ua;
@@ -520,11 +521,12 @@ int gemm_impl(int forced, int m, int n, int k, T alpha, const T* A, int lda, con
     if (forced >= count) return PGEMM_EVARIANT;
     idx = forced;
     if (table[idx].vec && !vec) return PGEMM_EVARIANT;
+    if (table[idx].max_ldc > 0 && ldc > table[idx].max_ldc) return PGEMM_EVARIANT;
   } else {
     // stream-K only where pick chose it: a workspace too small for the
     // preferred plan gives exactly the plain entry point's launch, even if
     // the fallback tiling's own plan would fit
-    idx = pick<T>(m, n, k, vec, ws != nullptr ? ws_bytes : 0, &plan, &strip);
+    idx = pick<T>(m, n, k, ldc, vec, ws != nullptr ? ws_bytes : 0, &plan, &strip);
   }
   return run(table[idx], m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, plan,
              static_cast<T*>(ws), strip, s);
@@ -552,11 +554,12 @@ void* scratch_address() {
   return ptrs[dev];
 }
 
-// Workspace the stream-K path would use for this shape (0: none).
+// Workspace the stream-K path would use for this shape (0: none), for any
+// ldc that every tile class takes.
 template <typename T>
 size_t workspace_impl(int m, int n, int k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
-  return choose<T>(m, n, k, true).plan.bytes;
+  return choose<T>(m, n, k, true, 0).plan.bytes;
 }
 
 template <typename T>
@@ -570,7 +573,7 @@ int select_impl(int m, int n, int k, T alpha, const T* A, int lda, const T* B, i
   const bool vec = vec_ok(A, lda, B, ldb, C, ldc);
   SkPlan plan;
   int strip = 0;
-  const int idx = pick<T>(m, n, k, vec, ws_bytes, &plan, &strip);
+  const int idx = pick<T>(m, n, k, ldc, vec, ws_bytes, &plan, &strip);
   if (sk_wgs != nullptr) *sk_wgs = plan.wgs;
   if (strip_rows_out != nullptr) *strip_rows_out = strip;
   if constexpr (sizeof(T) == 4) return 1 + idx;

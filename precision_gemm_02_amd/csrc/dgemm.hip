@@ -8,10 +8,12 @@
 
 namespace pgemm {
 
-// Threads per workgroup and the width limits of a configuration's own strip
-// workgroups (used where it computes strip rows in its grid; see strip_cols).
+// Threads per workgroup, the width limits of a configuration's own strip
+// workgroups (used where it computes strip rows in its grid; see strip_cols)
+// and the largest ldc it takes (0: any).
 #define PGEMM_STRIP_LIMITS(...) \
-  threads_of<__VA_ARGS__>(), strip_scmax_of<__VA_ARGS__>(), strip_acc_of<__VA_ARGS__>()
+  threads_of<__VA_ARGS__>(), strip_scmax_of<__VA_ARGS__>(), strip_acc_of<__VA_ARGS__>(), \
+      max_ldc_of<__VA_ARGS__>()
 
 #define PGEMM_F64(BM, BN, BK, WM, WN, S, VEC, SUFFIX)                                        \
   {"f64_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_s" #S "_" #SUFFIX, BM, BN, BK, VEC, false, false, \

@@ -220,6 +220,15 @@ struct TileCfg {
   // takes at most 64 registers.
   static constexpr bool PF_CT =
       !STAGED_EPI && KS == 1 && RB * CB * TR::NACC * (int)sizeof(T) / 4 <= 64;
+  // The fp32 64 x 64 class stores C written through to memory (cache policy
+  // sc0 sc1) rather than leaving its lines dirty in each XCD's L2: measured
+  // faster on every shape tried, with beta = 0 and beta != 0 (by up to 17 %
+  // at some leading dimensions; see the epilogue).  Its stores address C
+  // from the tile's first element with 32-bit byte offsets, so ldc is held to
+  // WT_MAX_LDC (the host does not launch this class beyond it).
+  static constexpr bool WT_C = sizeof(T) == 4 && BM == 64 && BN == 64 && KS == 1;
+  static constexpr long long WT_MAX_LDC =
+      WT_C ? (0x7fffffffLL / (long long)sizeof(T) - BM) / BN : 0;
   // When the grid also computes strip rows (one K group per strip
   // workgroup: its latency passes beside the tiles), the strip role's sums
   // per thread (at most STRIP_ACC elements, STRIP_SCMAX columns per wave)
@@ -335,6 +344,15 @@ __device__ __forceinline__ void load_chunk_buf_lds(__amdgpu_buffer_rsrc_t r, int
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, kBufferWord3);
+}
+
+// 16 bytes stored at byte offset voff from the descriptor's base, written
+// through to memory (cache policy sc0 sc1) instead of left dirty in L2.
+template <class TR>
+__device__ __forceinline__ void store_chunk_wt(__amdgpu_buffer_rsrc_t r, int voff,
+                                               typename TR::chunk_t v) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, voff, 0, 17);
 }
 
 // Host check for GemmArgs::buf32: the largest byte offset of a whole-tile
@@ -1302,6 +1320,24 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       static_assert(RUN % V == 0, "a run is whole 16-byte chunks");
       static_assert(NCH % 64 == 0, "whole chunks per lane");
       T* const stg = lds + wave_in * (MB * LDW);
+      // A whole chunk of C (or of the workspace slot) at (gcol, grow) of this
+      // frame.  Written through in the fp32 64 x 64 class (TileCfg::WT_C),
+      // from the frame's first element with 32-bit byte offsets.  Measured
+      // there on 1024^3 (workspace-free launches, back to back): -1.6 % with
+      // beta = 0 and -1.4 % with beta = 0.5; at 896^3 and 1000^3 with
+      // beta = 0.5 -9 % and -11 %, and -17 % at ldc 1280.  Ordinary stores
+      // cost an L2 write-back of C at the kernel's end, and with beta != 0
+      // at most leading dimensions a further ~3 us.  A run-time choice
+      // between the two at each store measured slower than either.
+      const int col0 = to_ws ? 0 : n0, row0 = to_ws ? 0 : m0;
+      auto put_chunk = [&](const int gcol, const int grow, const chunk_t& out)
+                           __attribute__((always_inline)) {
+        if constexpr (Cfg::WT_C)
+          store_chunk_wt<TR>(tile_rsrc(cbase + (size_t)col0 * ldc + row0),
+                             ((gcol - col0) * ldc + (grow - row0)) * (int)sizeof(T), out);
+        else
+          store_chunk<TR, VEC>(cbase + (size_t)gcol * ldc + grow, out);
+      };
       // With beta != 0 and the whole tile inside C, the old C of column block
       // c+1 is loaded as soon as block c is staged (its accumulators are free
       // then), so that its HBM latency passes while block c is stored; block
@@ -1369,8 +1405,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
             chunk_t out;
   #pragma unroll
             for (int e = 0; e < V; ++e) out[e] = fma_t(beta, cold[e], alpha * v[e]);
-            store_chunk<TR, VEC>(cbase + (size_t)(col_base + c * MB + col) * ldc + (row_base + rc * V),
-                                 out);
+            put_chunk(col_base + c * MB + col, row_base + rc * V, out);
           }
           __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the region is reused
           continue;
@@ -1393,7 +1428,7 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   #pragma unroll
                 for (int e = 0; e < V; ++e) out[e] = alpha * v[e];
               }
-              store_chunk<TR, VEC>(pc, out);
+              put_chunk(gcol, grow, out);
             } else {
   #pragma unroll
               for (int e = 0; e < V; ++e) {

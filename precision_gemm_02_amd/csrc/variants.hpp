@@ -20,6 +20,7 @@ struct Variant {
   LaunchFn<T> launch;
   int threads;     // per workgroup
   int strip_scmax, strip_acc;   // the grid's own strip role (see strip_cols)
+  long long max_ldc;   // largest ldc the configuration takes (0: any; see TileCfg::WT_MAX_LDC)
   // Columns per wave and column groups per workgroup of the strip of r rows
   // over n columns on `units` compute units: the grid's own strip role, or
   // the strip kernel's.
@@ -43,6 +44,10 @@ constexpr int strip_scmax_of() {
 template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS = 1>
 constexpr int strip_acc_of() {
   return TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>::STRIP_ACC;
+}
+template <class TR, int BM, int BN, int BK, int WGM, int WGN, bool VEC, int STAGES, int KS = 1>
+constexpr long long max_ldc_of() {
+  return TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>::WT_MAX_LDC;
 }
 
 // Launch one tile configuration.  Plain: one workgroup per BM x BN tile of
@@ -76,6 +81,11 @@ hipError_t launch_tile(const GemmArgs<typename TR::T>& a, hipStream_t stream) {
     g.strip_wgs = 0;
   }
   const int rest = tiles - g.full_tiles;
+  {
+    using Cfg = TileCfg<TR, BM, BN, BK, WGM, WGN, VEC, STAGES, KS>;
+    // stores of C with 32-bit offsets from the tile's first element
+    if (Cfg::WT_MAX_LDC > 0 && g.ldc > Cfg::WT_MAX_LDC) return hipErrorInvalidValue;
+  }
   g.buf32 = buffer_offsets_fit<T>(BM, BN, BK, g.lda, g.ldb) ? 1 : 0;
   void* args[] = {&g};
   const dim3 grid((unsigned)(g.full_tiles + g.sk_wgs + g.strip_wgs)),

@@ -160,6 +160,30 @@ def test_selection_by_shape_and_alignment():
     assert name_of(v).endswith("_ua")
 
 
+def test_64x64_class_ldc_limit():
+    """The fp32 64 x 64 tiles store C through a buffer descriptor at a tile's
+    first element with 32-bit byte offsets, which hold 64 columns of ldc up to
+    8388606 elements.  Beyond that the planner takes another class (with and
+    without a workspace), and the forced variant is refused before any
+    launch."""
+    lim = 8388606
+    v = pg.select_f32(1024, 1024, 1024, 1.0, FAKE, 1024, FAKE, 1024, 0.0, FAKE, lim - 2)
+    assert name_of(v) == "f32_64x64x16_w2x2_s4_vec"
+    for ldc in (lim + 2, 1 << 24):
+        v = pg.select_f32(1024, 1024, 1024, 1.0, FAKE, 1024, FAKE, 1024, 0.0, FAKE, ldc)
+        assert not name_of(v).startswith("f32_64x64x16"), (ldc, name_of(v))
+        e = (732, 316, 3260, 1.0, FAKE, 732, FAKE, 3260, 0.0, FAKE, ldc)
+        v, _, _ = pg.select_ws_f32(*e, pg.workspace_f32(*e[:3]))
+        assert not name_of(v).startswith("f32_64x64x16"), (ldc, name_of(v))
+    ids = {n: v for v, n in pg.variants().items()}
+    for name in ("f32_64x64x16_w2x2_s4_vec", "f32_64x64x16_w2x2_s4_ua"):
+        assert L.gemm_f32_variant(ids[name], 1024, 1024, 1024, 1.0, FAKE, 1024, FAKE, 1024,
+                                  0.0, FAKE, lim + 2, None) == pg.PGEMM_EVARIANT
+    # the two-K-group 64 x 64 class and the fp64 kernels have no such limit
+    v = pg.select_f32(1024, 1024, 8192, 1.0, FAKE, 1024, FAKE, 8192, 0.0, FAKE, 1 << 24)
+    assert name_of(v) == "f32_64x64x32_w2x2_s3_k2_vec"
+
+
 def test_selection_with_workspace():
     # 2150 x 2030 x 1000: with the workspace it asks for, 128 x 128 tiles (a
     # full round of 256 + 16) with 240 stream-K workgroups (15 per leftover
