@@ -220,13 +220,14 @@ struct TileCfg {
   // takes at most 64 registers.
   static constexpr bool PF_CT =
       !STAGED_EPI && KS == 1 && RB * CB * TR::NACC * (int)sizeof(T) / 4 <= 64;
-  // The fp32 64 x 64 class stores C written through to memory (cache policy
-  // sc0 sc1) rather than leaving its lines dirty in each XCD's L2: measured
-  // faster on every shape tried, with beta = 0 and beta != 0 (by up to 17 %
-  // at some leading dimensions; see the epilogue).  Its stores address C
-  // from the tile's first element with 32-bit byte offsets, so ldc is held to
-  // WT_MAX_LDC (the host does not launch this class beyond it).
-  static constexpr bool WT_C = sizeof(T) == 4 && BM == 64 && BN == 64 && KS == 1;
+  // The fp32 64 x 64 classes (one K group, and two) store C written through
+  // to memory (cache policy sc0 sc1) rather than leaving its lines dirty in
+  // each XCD's L2: measured faster on every shape tried, with beta = 0 and
+  // beta != 0 (one K group: by up to 17 % at some leading dimensions, see the
+  // epilogue; two: by up to 0.6 %).  Their stores address C from the tile's
+  // first element with 32-bit byte offsets, so ldc is held to WT_MAX_LDC
+  // (the host does not launch these classes beyond it).
+  static constexpr bool WT_C = sizeof(T) == 4 && BM == 64 && BN == 64 && KS <= 2;
   static constexpr long long WT_MAX_LDC =
       WT_C ? (0x7fffffffLL / (long long)sizeof(T) - BM) / BN : 0;
   // When the grid also computes strip rows (one K group per strip
@@ -1242,7 +1243,11 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
   #pragma unroll
             for (int e = 0; e < V; ++e) out[e] = alpha * v[e];
           }
-          store_chunk<TR, VEC>(pc, out);
+          if constexpr (Cfg::WT_C)
+            store_chunk_wt<TR>(tile_rsrc(cbase + (size_t)c0 * ldc + r0),
+                               ((gcol[i] - c0) * ldc + (grow[i] - r0)) * (int)sizeof(T), out);
+          else
+            store_chunk<TR, VEC>(pc, out);
         } else {
   #pragma unroll
           for (int e = 0; e < V; ++e) {

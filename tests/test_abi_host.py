@@ -161,7 +161,7 @@ def test_selection_by_shape_and_alignment():
 
 
 def test_64x64_class_ldc_limit():
-    """The fp32 64 x 64 tiles store C through a buffer descriptor at a tile's
+    """The fp32 64 x 64 tiles (one or two K groups) store C through a buffer descriptor at a tile's
     first element with 32-bit byte offsets, which hold 64 columns of ldc up to
     8388606 elements.  Beyond that the planner takes another class (with and
     without a workspace), and the forced variant is refused before any
@@ -179,9 +179,17 @@ def test_64x64_class_ldc_limit():
     for name in ("f32_64x64x16_w2x2_s4_vec", "f32_64x64x16_w2x2_s4_ua"):
         assert L.gemm_f32_variant(ids[name], 1024, 1024, 1024, 1.0, FAKE, 1024, FAKE, 1024,
                                   0.0, FAKE, lim + 2, None) == pg.PGEMM_EVARIANT
-    # the two-K-group 64 x 64 class and the fp64 kernels have no such limit
-    v = pg.select_f32(1024, 1024, 8192, 1.0, FAKE, 1024, FAKE, 8192, 0.0, FAKE, 1 << 24)
+    # the two-K-group 64 x 64 class stores C the same way
+    v = pg.select_f32(1024, 1024, 8192, 1.0, FAKE, 1024, FAKE, 8192, 0.0, FAKE, lim - 2)
     assert name_of(v) == "f32_64x64x32_w2x2_s3_k2_vec"
+    v = pg.select_f32(1024, 1024, 8192, 1.0, FAKE, 1024, FAKE, 8192, 0.0, FAKE, 1 << 24)
+    assert not name_of(v).startswith("f32_64x64"), name_of(v)
+    for name in ("f32_64x64x32_w2x2_s3_k2_vec", "f32_64x64x32_w2x2_s3_k2_ua"):
+        assert L.gemm_f32_variant(ids[name], 1024, 1024, 8192, 1.0, FAKE, 1024, FAKE, 8192,
+                                  0.0, FAKE, lim + 2, None) == pg.PGEMM_EVARIANT
+    # other classes take any ldc
+    v = pg.select_f32(2048, 2048, 2048, 1.0, FAKE, 2048, FAKE, 2048, 0.0, FAKE, 1 << 24)
+    assert name_of(v).startswith("f32_128x128")
 
 
 def test_selection_with_workspace():
