@@ -211,10 +211,10 @@ const char *pgemm_status_string(int status);
  * forced variant (same contract as gemm_f32 / gemm_f64, plus
  * PGEMM_EVARIANT for an unknown id, one of the other precision, an aligned
  * ("vec") variant with unaligned arguments, or an ldc beyond the variant's
- * limit: the fp32 64 x 64 variants (one or two K groups) store C with 32-bit
- * offsets from a tile's first element and take ldc <= 8388606; gemm_f32
- * does not choose them beyond that); they let tests cover every compiled
- * tile configuration.
+ * limit: the 64 x 64 variants store C with 32-bit offsets from a tile's
+ * first element and take ldc <= 8388606 (fp32) or 4194302 (fp64); gemm_f32
+ * and gemm_f64 do not choose them beyond that); they let tests cover every
+ * compiled tile configuration.
  */
 int pgemm_select_f32(int m, int n, int k, float alpha, const float *A, int lda,
                      const float *B, int ldb, float beta, const float *C, int ldc);

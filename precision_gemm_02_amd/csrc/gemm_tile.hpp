@@ -220,14 +220,15 @@ struct TileCfg {
   // takes at most 64 registers.
   static constexpr bool PF_CT =
       !STAGED_EPI && KS == 1 && RB * CB * TR::NACC * (int)sizeof(T) / 4 <= 64;
-  // The fp32 64 x 64 classes (one K group, and two) store C written through
-  // to memory (cache policy sc0 sc1) rather than leaving its lines dirty in
-  // each XCD's L2: measured faster on every shape tried, with beta = 0 and
-  // beta != 0 (one K group: by up to 17 % at some leading dimensions, see the
-  // epilogue; two: by up to 0.6 %).  Their stores address C from the tile's
-  // first element with 32-bit byte offsets, so ldc is held to WT_MAX_LDC
-  // (the host does not launch these classes beyond it).
-  static constexpr bool WT_C = sizeof(T) == 4 && BM == 64 && BN == 64 && KS <= 2;
+  // The 64 x 64 classes (fp32 with one K group or two, fp64) store C
+  // written through to memory (cache policy sc0 sc1) rather than leaving its
+  // lines dirty in each XCD's L2.  Measured faster on the shapes they serve,
+  // with beta = 0 and beta != 0: fp32 with one K group by up to 17 % at some
+  // leading dimensions (see the staged epilogue), two K groups by up to
+  // 0.6 %, fp64 by 1-2 % on single rounds.  Their stores address C from the
+  // tile's first element with 32-bit byte offsets, so ldc is held to
+  // WT_MAX_LDC (the host does not launch these classes beyond it).
+  static constexpr bool WT_C = BM == 64 && BN == 64 && KS <= 2;
   static constexpr long long WT_MAX_LDC =
       WT_C ? (0x7fffffffLL / (long long)sizeof(T) - BM) / BN : 0;
   // When the grid also computes strip rows (one K group per strip
@@ -1450,7 +1451,8 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
       }
     } else {
       // Direct stores from the accumulator registers: runs of RUN rows of a
-      // column per lane, 16-byte stores where whole chunks.
+      // column per lane, 16-byte stores where whole chunks (written through,
+      // from the frame's first element, in the 64 x 64 class: TileCfg::WT_C).
       const bool full_out = to_ws || full_mn;
       const int row_off = to_ws ? 0 : m0, col_off = to_ws ? 0 : n0;
       constexpr bool VEC_C = (RUN % V == 0);   // whole 16-byte chunks per run
@@ -1494,7 +1496,13 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
                 chunk_t v;
   #pragma unroll
                 for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
-                store_chunk<TR, VEC>(pc + h * V, v);
+                if constexpr (Cfg::WT_C)
+                  store_chunk_wt<TR>(tile_rsrc(cbase + (size_t)col_off * ldc + row_off),
+                                     (int)((pc + h * V) - (cbase + (size_t)col_off * ldc + row_off)) *
+                                         (int)sizeof(T),
+                                     v);
+                else
+                  store_chunk<TR, VEC>(pc + h * V, v);
               }
             } else {
   #pragma unroll
@@ -1551,7 +1559,13 @@ gemm_tile_kernel(GemmArgs<typename TR::T> g) {
                   chunk_t v;
   #pragma unroll
                   for (int e = 0; e < V; ++e) v[e] = out[h * V + e];
-                  store_chunk<TR, VEC>(pc + h * V, v);
+                  if constexpr (Cfg::WT_C)
+                    store_chunk_wt<TR>(tile_rsrc(cbase + (size_t)col_off * ldc + row_off),
+                                       (int)((pc + h * V) - (cbase + (size_t)col_off * ldc + row_off)) *
+                                           (int)sizeof(T),
+                                       v);
+                  else
+                    store_chunk<TR, VEC>(pc + h * V, v);
                 }
               } else {
   #pragma unroll

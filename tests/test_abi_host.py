@@ -161,9 +161,9 @@ def test_selection_by_shape_and_alignment():
 
 
 def test_64x64_class_ldc_limit():
-    """The fp32 64 x 64 tiles (one or two K groups) store C through a buffer descriptor at a tile's
-    first element with 32-bit byte offsets, which hold 64 columns of ldc up to
-    8388606 elements.  Beyond that the planner takes another class (with and
+    """The 64 x 64 tiles (fp32 with one or two K groups, fp64) store C through
+    a buffer descriptor at a tile's first element with 32-bit byte offsets,
+    which hold 64 columns of ldc up to 8388606 fp32 or 4194302 fp64 elements.  Beyond that the planner takes another class (with and
     without a workspace), and the forced variant is refused before any
     launch."""
     lim = 8388606
@@ -190,6 +190,15 @@ def test_64x64_class_ldc_limit():
     # other classes take any ldc
     v = pg.select_f32(2048, 2048, 2048, 1.0, FAKE, 2048, FAKE, 2048, 0.0, FAKE, 1 << 24)
     assert name_of(v).startswith("f32_128x128")
+    # fp64 64 x 64 tiles: 64 columns of 8-byte elements, ldc up to 4194302
+    lim64 = 4194302
+    v = pg.select_f64(1024, 1024, 1024, 1.0, FAKE, 1024, FAKE, 1024, 1.0, FAKE, lim64)
+    assert name_of(v) == "f64_64x64x16_w2x4_s4_vec"
+    v = pg.select_f64(1024, 1024, 1024, 1.0, FAKE, 1024, FAKE, 1024, 1.0, FAKE, lim64 + 2)
+    assert not name_of(v).startswith("f64_64x64"), name_of(v)
+    assert L.gemm_f64_variant(ids["f64_64x64x16_w2x4_s4_ua"], 1024, 1024, 1024,
+                              ctypes.c_double(1.0), FAKE, 1024, FAKE, 1024, ctypes.c_double(1.0),
+                              FAKE, lim64 + 1, None) == pg.PGEMM_EVARIANT
 
 
 def test_selection_with_workspace():
