@@ -136,7 +136,9 @@ struct Tables {
     // of one tile, ~3.5 us fixed in all; 640^3 8.7 us against 11.9 for
     // 64 x 64 tiles, 1024 x 512 x 1024 11.7 against 17.3, but 1024^3 24.0
     // against 17.8 (four tiles per compute unit: their operand traffic then
-    // bounds them), so beyond three tiles per unit it is priced by rounds.  A lone
+    // bounds them).  Beyond three tiles per unit it is priced in groups of
+    // three per unit (see estimate: up to three groups, with K loops of 12 K
+    // tiles or more; otherwise by rounds).  A lone
     // tile per unit with a long K loop (8 K tiles or more) runs at 0.5 to
     // 0.8: 768 x 64 x 2836 22.9 us (panels shared by 2 tiles), 252^2 x 4096
     // 27.9 (columns of 1008 bytes), 256^2 x 4096 20.1.  It is priced at 0.5,
@@ -302,6 +304,24 @@ double estimate(const Variant<T>& v, const TileClass& tc, int m, int n, int k, i
   if (tc.coresident > 0 && per_cu <= tc.coresident) {
     const bool lone = per_cu == 1 && k >= 8 * v.bk;
     return fixed + kloop * (double)per_cu * (lone ? tc.eff / tc.eff_lone : 1.0);
+  }
+  if (tc.coresident > 0 && per_cu <= 3 * tc.coresident && k >= 12 * v.bk &&
+      (sk == nullptr || sk->wgs == 0)) {
+    // more tiles than run together, up to three groups, K loops of 12 K
+    // tiles or more: groups of `coresident` tiles per unit, each one fixed
+    // part plus their K loops, the last group partly filled (measured on 18
+    // shapes whose choice this changes: 2 to 22 % faster on 15; at ~20 tiles
+    // per unit the small tiles' memory traffic made them 8 % slower, and
+    // with 8 K tiles their fixed costs 9 %)
+    const long long group = (long long)cus * tc.coresident;
+    const long long full = tiles / group, rest_g = tiles - full * group;
+    double t = (double)full * (fixed + kloop * (double)tc.coresident);
+    if (rest_g > 0) {
+      const long long last = ceil_div(rest_g, (long long)cus);
+      const bool lone = last == 1 && k >= 8 * v.bk;
+      t += fixed + kloop * (double)last * (lone ? tc.eff / tc.eff_lone : 1.0);
+    }
+    return t;
   }
   const double t = (double)rounds * (kloop + fixed);
   if (rest == 0) return t;

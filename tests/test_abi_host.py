@@ -136,7 +136,8 @@ def test_selection_by_shape_and_alignment():
     assert name_of(v) == "f32_64x64x32_w2x2_s3_k2_ua"
     # 32 x 32 tiles in four K groups: small problems, and up to three tiles
     # per compute unit, which run together (640^3: 400 tiles; 768^3: 576);
-    # four or more per unit are priced by rounds (896^3: 784 tiles)
+    # four or more per unit are priced in groups of three per unit, which
+    # still leaves 896^3 (784 tiles) and 1024^3 (1024) to 64 x 64 tiles
     for n in (128, 512, 640, 768):
         v = pg.select_f32(n, n, n, 1.0, FAKE, n, FAKE, n, 0.0, FAKE, n)
         assert name_of(v) == "f32_32x32x64_w1x1_s3_k4_vec", (n, name_of(v))
