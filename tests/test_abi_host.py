@@ -143,6 +143,16 @@ def test_selection_by_shape_and_alignment():
         assert name_of(v) == "f32_32x32x64_w1x1_s3_k4_vec", (n, name_of(v))
     v = pg.select_f32(896, 896, 896, 1.0, FAKE, 896, FAKE, 896, 0.0, FAKE, 896)
     assert name_of(v) == "f32_64x64x16_w2x2_s4_vec"
+    # 4 to 9 of them per unit with K loops of 12 K tiles or more are priced in
+    # groups of three per unit: 1152^3 (1296 tiles) and 1100 x 1000 x 900 run
+    # as 32 x 32 tiles (measured 10-16 % faster than 64 x 64); ~20 per unit
+    # (2924 x 1760 x 4292) or 8 K tiles (3192 x 460 x 516) keep larger tiles
+    for e in ((1152, 1152, 1152), (1100, 1000, 900)):
+        v = pg.select_f32(*e, 1.0, FAKE, e[0], FAKE, e[2], 0.0, FAKE, e[0])
+        assert name_of(v) == "f32_32x32x64_w1x1_s3_k4_vec", (e, name_of(v))
+    for e in ((2924, 1760, 4292), (3192, 460, 516)):
+        v = pg.select_f32(*e, 1.0, FAKE, e[0], FAKE, e[2], 0.0, FAKE, e[0])
+        assert not name_of(v).startswith("f32_32x32"), (e, name_of(v))
     # one such tile per unit with a long K loop is priced low enough that
     # stream-K of 64 x 64 tiles takes it where a workspace allows
     e = (732, 316, 3260, 1.0, FAKE, 732, FAKE, 3260, 0.0, FAKE, 732)
